@@ -1,0 +1,197 @@
+/*
+ * specverify.h -- C ABI of libspecverify: batched speculative-decoding
+ * verification (rejection sampling with residual / bonus resampling) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method (cited by page and section):
+ *   [Primer] "猜想解码 (Speculative Decoding) 全景" (talentme.airsota.com):
+ *     考点 1  - the target model scores gamma+1 positions in one pass;
+ *     考点 2  - accept a drafted token x with probability
+ *               min(1, p_target(x) / p_draft(x)); on rejection draw from the
+ *               residual max(0, p_target - p_draft) / sum;
+ *     考点 4  - every step yields at least one token; all gamma accepted
+ *               yields gamma + 1 (the extra, "bonus", token);
+ *     第二章 / 第三章 - the same acceptance rule per position.
+ *   [Edge] lqnn.cn/news/249899, "动态推迟投机验证调度器设计": probabilities
+ *     are softmax(logits / T) with one temperature T for both models; the
+ *     pipeline figure in "嵌入式流式推理的访存墙与投机瓶颈" places an
+ *     accept/reject evaluation kernel after a batched target pass over a
+ *     token tree.
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers owned by the caller. The
+ *     library never allocates, frees or retains them, and keeps no per-call
+ *     state; scratch memory is the caller's `workspace`.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
+ *     stream). Outputs are valid after the caller synchronises that stream.
+ *   - Logits are row-major with the vocabulary contiguous; `dtype` is
+ *     SV_F32 (float) or SV_BF16 (bfloat16 bit patterns, uint16). Target and
+ *     draft share one dtype. Pointers must be aligned to the element size;
+ *     rows need not be 16-byte aligned.
+ *   - Temperature is per request (float). T == 0 selects greedy decoding:
+ *     accept while the draft token equals the target argmax (lowest index on
+ *     ties) and emit the argmax at the first mismatch; draft logits and the
+ *     uniforms of that request are not read.
+ *   - The random numbers of the method are inputs: u_accept decides the
+ *     acceptance test u * p_draft(x) < p_target(x) (equivalently
+ *     u < min(1, p_target/p_draft)); u_sample drives the inverse-CDF draw
+ *     y = min{ j : C_j > u * S } over the residual (or bonus) masses in
+ *     ascending token order. Uniforms must lie in [0, 1).
+ *   - num_accepted counts accepted draft tokens (0..gamma); the request emits
+ *     num_accepted + 1 tokens; later columns of out_tokens are -1.
+ *   - Host-side argument errors return a negative sv_status before anything
+ *     is enqueued. Per-request data errors (temperature NaN, negative,
+ *     infinite or subnormal; a token outside [0, V); for T > 0 a uniform NaN
+ *     or outside [0, 1); a logit row that is read and holds a NaN, a +inf or
+ *     no finite value; for the ragged and tree layouts a malformed layout)
+ *     are reported on the device: num_accepted = -1 and that request's
+ *     out_tokens row filled with -1. No call synchronises the stream.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sv_status {
+    SV_OK = 0,
+    SV_EINVAL = -1,  /* null pointer, bad size or count                        */
+    SV_EDTYPE = -2,  /* dtype not SV_F32 / SV_BF16                              */
+    SV_ENOWS = -3,   /* workspace null, too small or not 256-byte aligned       */
+    SV_EALIGN = -4,  /* a logits pointer not aligned to its element size        */
+    SV_EHIP = -5,    /* a HIP runtime call or kernel launch failed              */
+} sv_status;
+
+typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Largest sizes accepted (host-side validation). */
+#define SV_MAX_GAMMA 1024      /* drafted positions per request          */
+#define SV_MAX_TREE_NODES 1024 /* nodes per token tree (root included)    */
+#define SV_MAX_VOCAB (1 << 28)
+
+/* Workspace bytes needed by spec_verify for these sizes (0 on bad sizes). */
+size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t dtype);
+
+/*
+ * Linear (chain) verification of B requests with gamma drafted tokens each
+ * [Primer 考点1, 考点2, 考点4].
+ *   target_logits  [B, gamma+1, V]  row i = target distribution at position i
+ *   draft_logits   [B, gamma,   V]  row i = distribution draft token i came from
+ *   draft_tokens   [B, gamma]  int32
+ *   u_accept       [B, gamma]  float, uniform for the test at position i
+ *   u_sample       [B, gamma+1] float, uniform for the draw at the final
+ *                  position n (residual if n < gamma, bonus if n == gamma)
+ *   temperature    [B] float
+ *   out_tokens     [B, gamma+1] int32 (written)
+ *   num_accepted   [B] int32 (written)
+ *   diag_probs     [B, gamma, 2] float or NULL: (p_target(x_i), p_draft(x_i))
+ *                  for T > 0 requests (NaN otherwise); for parity checks.
+ *   workspace      >= spec_verify_workspace_bytes(B, gamma, V, dtype) bytes,
+ *                  256-byte aligned; contents need no initialisation.
+ * B == 0 is a no-op. Errors: SV_EINVAL (B < 0, gamma outside [0,
+ * SV_MAX_GAMMA], V outside [1, SV_MAX_VOCAB], a required pointer NULL),
+ * SV_EDTYPE, SV_EALIGN, SV_ENOWS, SV_EHIP.
+ */
+int spec_verify(const void* target_logits, const void* draft_logits, int32_t dtype,
+                const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                const float* temperature, int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
+                int32_t* num_accepted, float* diag_probs, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Workspace bytes for spec_verify_ragged. */
+size_t spec_verify_ragged_workspace_bytes(int32_t B, int32_t total_draft, int32_t gamma_max, int32_t V,
+                                          int32_t dtype);
+
+/*
+ * Ragged (mixed gamma and temperature) verification [Primer 考点1, 考点2,
+ * 考点4]: request b owns gamma_b = cu_gamma[b+1] - cu_gamma[b] drafted
+ * positions, draft rows cu_gamma[b] .. cu_gamma[b+1]-1 and target rows
+ * cu_gamma[b]+b .. cu_gamma[b+1]+b.
+ *   target_logits  [total_draft + B, V]     draft_logits [total_draft, V]
+ *   cu_gamma       [B+1] int32, device     total_draft  host copy of cu_gamma[B]
+ *   draft_tokens, u_accept [total_draft]   u_sample [total_draft + B]
+ *   temperature    [B]
+ *   out_tokens     [B, gamma_max+1]         num_accepted [B]
+ *   diag_probs     [total_draft, 2] or NULL
+ * The layout is valid when cu_gamma[0] == 0, it never decreases, every
+ * gamma_b <= gamma_max and cu_gamma[B] == total_draft; otherwise every
+ * request reports -1.
+ */
+int spec_verify_ragged(const void* target_logits, const void* draft_logits, int32_t dtype,
+                       const int32_t* cu_gamma, int32_t total_draft, const int32_t* draft_tokens,
+                       const float* u_accept, const float* u_sample, const float* temperature, int32_t B,
+                       int32_t gamma_max, int32_t V, int32_t* out_tokens, int32_t* num_accepted,
+                       float* diag_probs, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for spec_verify_tree. */
+size_t spec_verify_tree_workspace_bytes(int32_t B, int32_t N, int32_t V, int32_t dtype);
+
+/*
+ * Token-tree verification [Primer 考点3: multi-head drafts verified as a
+ * tree in one target pass; Edge pipeline figure: token tree -> accept/reject
+ * evaluation]. Node 0 is the root (already emitted context); node v >= 1
+ * carries draft token node_tokens[v] and parent parents[v] < v.
+ *   target_logits  [B, N, V]   row v = target distribution after the path to v
+ *   draft_logits   [B, N-1, V] row v-1 = distribution node v's token came from
+ *   node_tokens, parents, u_accept, u_sample [B, N] int32/float
+ *   out_tokens, out_nodes [B, max_depth+1]; num_accepted [B]
+ * Node v is accepted when u_accept[v] * p_draft[v](x_v) < p_target[parent(v)](x_v)
+ * (greedy: x_v == argmax of the parent's target row); a node is kept when it
+ * and all its ancestors are accepted; the end node e is the deepest kept node
+ * (lowest index on ties). out_tokens holds the tokens of the path root->e
+ * (root excluded) and then one drawn token with u_sample[e]: from p_target[e]
+ * when e has no children, else from the residual of p_target[e] against the
+ * draft row of e's lowest-index child. out_nodes holds the path's node
+ * indices. A tree with parents[0] != -1, a parent index >= its child, or a
+ * depth above max_depth reports -1 for that request.
+ */
+int spec_verify_tree(const void* target_logits, const void* draft_logits, int32_t dtype,
+                     const int32_t* node_tokens, const int32_t* parents, const float* u_accept,
+                     const float* u_sample, const float* temperature, int32_t B, int32_t N, int32_t V,
+                     int32_t max_depth, int32_t* out_tokens, int32_t* out_nodes, int32_t* num_accepted,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for spec_row_softmax_stats. */
+size_t spec_row_softmax_stats_workspace_bytes(int32_t rows, int32_t V, int32_t dtype);
+
+/*
+ * Per-row softmax statistics, the first stage of every verify call
+ * [Edge scheduler section: max and sum of exp((l - max)/T) per row]:
+ *   logits [rows, V], temperature [rows]
+ *   out_max    [rows] float: the row maximum
+ *   out_logz   [rows] float: log sum_j exp((l_j - max)/T) for T > 0, else NaN
+ *   out_argmax [rows] int32: lowest index of the maximum for T == 0, else -1
+ * Unusable rows report out_max = NaN. Exposed for parity checks of the
+ * streaming reduction on its own.
+ */
+int spec_row_softmax_stats(const void* logits, int32_t dtype, int32_t rows, int32_t V,
+                           const float* temperature, float* out_max, float* out_logz, int32_t* out_argmax,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable text for an sv_status. */
+const char* spec_verify_strerror(int status);
+
+/* Library ABI version. */
+int spec_verify_version(void);
+
+/*
+ * Optional timing of the streaming row-statistics kernel inside the calls
+ * above: when enabled, each call records a pair of HIP events around that
+ * kernel on `stream`. spec_verify_timing_read returns the per-call durations
+ * (ms) recorded since enabling, after the caller synchronised the stream; at
+ * most `max` values are written and *count receives how many are available.
+ * Enabling creates the events (host-side allocation), so it is not meant for
+ * callers that forbid allocation. Not thread-safe.
+ */
+int spec_verify_timing_enable(int enable);
+int spec_verify_timing_read(float* ms_out, int32_t max, int32_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -140,7 +140,7 @@ def sample_tokens(seed, rows, T_per_row, row_key, stream=S_TOKENS):
 def chain_inputs(B, gamma, V, seed, *, dtype="f32", dist=DIST_NORMAL, scale=1.0, n_spikes=0,
                  spike_height=0.0, noise_sd=0.7, temperature=1.0):
     """Dense chain batch: target [B, g+1, V], draft [B, g, V], tokens/u_accept [B, g], u_sample [B, g+1]."""
-    T = np.ascontiguousarray(np.broadcast_to(np.asarray(temperature, np.float32), (B,)))
+    T = np.array(np.broadcast_to(np.asarray(temperature, np.float32), (B,)), dtype=np.float32)
     sd = np.broadcast_to(np.asarray(noise_sd, np.float64), (B,))
     trow = np.arange(B * (gamma + 1), dtype=np.int64)
     target = logit_rows(seed, V, trow, dist=dist, scale=scale, n_spikes=n_spikes, spike_height=spike_height,
@@ -232,7 +232,7 @@ def tree_inputs(B, V, seed, *, n_nodes=64, fanout=(4, 4, 3), dtype="bf16", scale
     depth = np.zeros((B, N), np.int32)
     for v in range(1, N):
         depth[:, v] = depth[np.arange(B), parents[:, v]] + 1
-    T = np.ascontiguousarray(np.broadcast_to(np.asarray(temperature, np.float32), (B,)))
+    T = np.array(np.broadcast_to(np.asarray(temperature, np.float32), (B,)), dtype=np.float32)
     target = logit_rows(seed, V, np.arange(B * N, dtype=np.int64), scale=scale, dtype=dtype)
     b = np.repeat(np.arange(B), N - 1)
     v = np.tile(np.arange(1, N), B)

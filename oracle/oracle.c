@@ -395,6 +395,19 @@ typedef struct {
     double *pt_diag, *pd_diag, *acc_margin, *cdf_margin;
 } chain_batch;
 
+/* The packed layout describes the whole batch: it is usable only when
+ * cu[0] == 0, cu never decreases, every gamma_b <= gamma_max and
+ * cu[B] == total_draft; otherwise no request can be located reliably. */
+static int ragged_layout_valid(const int32_t *cu, int B, int gamma_max, int total_draft)
+{
+    if (cu[0] != 0 || cu[B] != total_draft)
+        return 0;
+    for (int b = 0; b < B; ++b)
+        if (cu[b + 1] < cu[b] || cu[b + 1] - cu[b] > gamma_max)
+            return 0;
+    return 1;
+}
+
 static void chain_task(void *p, int b, double *work)
 {
     const chain_batch *cb = (const chain_batch *)p;
@@ -405,7 +418,7 @@ static void chain_task(void *p, int b, double *work)
     size_t d0;
     if (cb->cu) {
         int lo = cb->cu[b], hi = cb->cu[b + 1];
-        if (lo < 0 || hi < lo || hi > cb->total_draft || hi - lo > cb->gamma) {
+        if (!ragged_layout_valid(cb->cu, cb->B, cb->gamma, cb->total_draft)) {
             fail_request(cb->out + (size_t)b * width, width, cb->num_accepted + b);
             cb->acc_margin[b] = cb->cdf_margin[b] = INFINITY;
             return;

@@ -1,0 +1,352 @@
+// accept.hip -- acceptance scan per request.
+//
+// Chain [Primer 考点2 / 第二章]: for drafted position i the token x_i is
+// accepted when u_accept[i] * p_d,i(x_i) < p_t,i(x_i), i.e. with probability
+// min(1, p_t/p_d); the first rejected position n ends the scan. Greedy
+// requests (T == 0) accept while x_i equals the target argmax and emit the
+// argmax at n. Token trees [Primer 考点3; Edge pipeline figure]: each node is
+// tested against its parent's target row; the kept nodes are those accepted
+// together with all their ancestors; the end node is the deepest kept node.
+// p(x) = 2^{(l_x - m) c} / Z with the row statistics merged here in fp64.
+#include "sv_internal.h"
+
+namespace sv {
+
+struct RowStat {
+  float m;   // row max
+  double Z;  // sum 2^{(x-m)c32}
+  int idx;   // greedy argmax
+  bool ok;
+};
+
+__device__ __forceinline__ RowStat merge_row(const Partial* __restrict__ p, int nchunk, float c32, bool greedy) {
+  float M = -INFINITY;
+  int idx = -1;
+  bool nan = false;
+  for (int k = 0; k < nchunk; ++k) {
+    Partial q = p[k];
+    nan |= q.s != q.s;
+    if (q.m > M) { M = q.m; idx = q.idx; }
+  }
+  RowStat r{M, 0.0, idx, !nan && M > -INFINITY && M < INFINITY};
+  if (greedy || !r.ok) return r;
+  double c = (double)c32, Z = 0.0;
+  for (int k = 0; k < nchunk; ++k) {
+    Partial q = p[k];
+    if (q.m > -INFINITY) Z += (double)q.s * exp2_f64(((double)q.m - (double)M) * c);
+  }
+  r.Z = Z;
+  r.ok = Z > 0.0 && Z < 1e308;
+  return r;
+}
+
+// probability of token x in a row with statistics st
+template <int DT>
+__device__ __forceinline__ double prob_at(const void* base, long long row, int V, int x, const RowStat& st, float c32) {
+  float l = Elem<DT>::at(base, row * (long long)V + x);
+  return exp2_f64(((double)l - (double)st.m) * (double)c32) / st.Z;
+}
+
+constexpr int kMaxPos = 1025;  // SV_MAX_GAMMA + 1
+
+template <int DT>
+__global__ __launch_bounds__(64) void k_accept_chain(const void* __restrict__ tgt, const void* __restrict__ dft, int V,
+                                                     Layout L, const int32_t* __restrict__ tokens,
+                                                     const float* __restrict__ ua, const float* __restrict__ us,
+                                                     const float* __restrict__ temperature,
+                                                     const Partial* __restrict__ part, int nchunk,
+                                                     int32_t* __restrict__ out, int out_width,
+                                                     int32_t* __restrict__ num_acc, float* __restrict__ diag,
+                                                     SampleJob* __restrict__ jobs) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  __shared__ float s_pt[kMaxPos], s_pd[kMaxPos];
+  __shared__ int s_amax[kMaxPos];
+
+  // --- locate the request's rows
+  bool layout_ok = true;
+  int g;
+  long long t0, d0;
+  if (L.mode == LAYOUT_RAGGED) {
+    const int32_t* cu = L.cu;
+    bool ok = true;
+    if (lane == 0) ok = cu[0] == 0 && cu[L.B] == L.total_draft;
+    for (int k = lane; k < L.B; k += 64) {
+      int lo = cu[k], hi = cu[k + 1];
+      ok = ok && hi >= lo && hi - lo <= L.gamma;
+    }
+    layout_ok = __all(ok);
+    g = layout_ok ? cu[b + 1] - cu[b] : 0;
+    d0 = layout_ok ? cu[b] : 0;
+    t0 = d0 + b;
+  } else {
+    g = L.gamma;
+    d0 = (long long)b * g;
+    t0 = (long long)b * (g + 1);
+  }
+  int32_t* orow = out + (long long)b * out_width;
+  const float T = temperature[b];
+  bool bad = !layout_ok || !temperature_ok(T);
+  const bool greedy = T == 0.0f;
+  const float c32 = bad || greedy ? 0.0f : c32_of(T);
+
+  // --- pass A: validation and acceptance decisions
+  int n = g;  // first rejected position
+  for (int base = 0; base <= g && !bad; base += 64) {
+    const int i = base + lane;
+    bool lbad = false, reject = false;
+    if (i <= g) {
+      RowStat st = merge_row(part + (t0 + i) * nchunk, nchunk, c32, greedy);
+      lbad |= !st.ok;
+      if (!greedy) lbad |= !uniform_ok(us[t0 + i]);
+      if (i < g) {
+        const int x = tokens[d0 + i];
+        lbad |= x < 0 || x >= V;
+        if (greedy) {
+          reject = x != st.idx;
+        } else {
+          RowStat sd = merge_row(part + (L.RT + d0 + i) * nchunk, nchunk, c32, false);
+          const float u = ua[d0 + i];
+          lbad |= !sd.ok || !uniform_ok(u);
+          if (!lbad) {
+            double pt = prob_at<DT>(tgt, t0 + i, V, x, st, c32);
+            double pd = prob_at<DT>(dft, d0 + i, V, x, sd, c32);
+            reject = !((double)u * pd < pt);
+            s_pt[i] = (float)pt;
+            s_pd[i] = (float)pd;
+          }
+        }
+      }
+      if (greedy) s_amax[i] = st.idx;
+    }
+    bad = __any(lbad) || bad;
+    unsigned long long rm = __ballot(reject && i < g);
+    if (rm && n == g) n = min(g, base + __builtin_ctzll(rm));
+  }
+  __syncthreads();
+
+  // --- outputs
+  if (bad) {
+    for (int k = lane; k < out_width; k += 64) orow[k] = -1;
+    if (lane == 0) {
+      num_acc[b] = -1;
+      jobs[b].kind = JOB_NONE;
+    }
+    return;
+  }
+  for (int k = lane; k < out_width; k += 64) {
+    int v = -1;
+    if (k < n) v = tokens[d0 + k];
+    else if (k == n && greedy) v = s_amax[n];
+    orow[k] = v;
+  }
+  if (diag)
+    for (int i = lane; i < g; i += 64) {
+      const float qnan = __uint_as_float(0x7fc00000u);
+      diag[2 * (d0 + i)] = greedy ? qnan : s_pt[i];
+      diag[2 * (d0 + i) + 1] = greedy ? qnan : s_pd[i];
+    }
+  if (lane == 0) {
+    num_acc[b] = n;
+    SampleJob J;
+    J.kind = greedy ? JOB_NONE : (n < g ? JOB_RESIDUAL : JOB_BONUS);
+    J.pos = n;
+    J.trow = t0 + n;
+    J.drow = d0 + n;
+    J.c64 = greedy ? 0.0 : c64_of(T);
+    J.u = greedy ? 0.0f : us[t0 + n];
+    J.rho = 0.0;
+    J.mt = J.md = 0.0f;
+    J.pad = 0;
+    if (!greedy) {
+      RowStat st = merge_row(part + (t0 + n) * nchunk, nchunk, c32, false);
+      J.mt = st.m;
+      if (n < g) {
+        RowStat sd = merge_row(part + (L.RT + d0 + n) * nchunk, nchunk, c32, false);
+        J.md = sd.m;
+        J.rho = st.Z / sd.Z;
+      }
+    }
+    jobs[b] = J;
+  }
+}
+
+hipError_t launch_accept_chain(int dt, const void* tgt, const void* dft, int V, const Layout& L,
+                               const int32_t* tokens, const float* ua, const float* us, const float* temperature,
+                               const Partial* part, int nchunk, int32_t* out, int out_width, int32_t* num_acc,
+                               float* diag, SampleJob* jobs, hipStream_t st) {
+  if (L.B == 0) return hipSuccess;
+  if (dt == 1)
+    hipLaunchKernelGGL(k_accept_chain<1>, dim3(L.B), dim3(64), 0, st, tgt, dft, V, L, tokens, ua, us, temperature,
+                       part, nchunk, out, out_width, num_acc, diag, jobs);
+  else
+    hipLaunchKernelGGL(k_accept_chain<0>, dim3(L.B), dim3(64), 0, st, tgt, dft, V, L, tokens, ua, us, temperature,
+                       part, nchunk, out, out_width, num_acc, diag, jobs);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Token trees: one workgroup per request, one thread per node.
+
+constexpr int kMaxNodes = 1024;
+
+template <int DT>
+__global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
+    const void* __restrict__ tgt, const void* __restrict__ dft, int V, Layout L, int max_depth,
+    const int32_t* __restrict__ tokens, const int32_t* __restrict__ parents, const float* __restrict__ ua,
+    const float* __restrict__ us, const float* __restrict__ temperature, const Partial* __restrict__ part,
+    int nchunk, int32_t* __restrict__ out, int32_t* __restrict__ out_nodes, int32_t* __restrict__ num_acc,
+    SampleJob* __restrict__ jobs) {
+  const int N = L.gamma;
+  const int b = blockIdx.x, v = threadIdx.x;
+  const int width = max_depth + 1;
+  __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_depth[2][kMaxNodes], s_ok[2][kMaxNodes];
+  __shared__ float s_mt[kMaxNodes];
+  __shared__ double s_zt[kMaxNodes];
+  __shared__ int s_idx[kMaxNodes];
+  __shared__ int s_bad;
+  __shared__ unsigned long long s_best;
+  __shared__ int s_child;
+
+  const float T = temperature[b];
+  const bool greedy = T == 0.0f;
+  const bool t_ok = temperature_ok(T);
+  const float c32 = (!t_ok || greedy) ? 0.0f : c32_of(T);
+  const long long t0 = (long long)b * N, d0 = (long long)b * (N - 1);
+  if (v == 0) { s_bad = t_ok ? 0 : 1; s_best = 0ull; s_child = 0x7fffffff; }
+  __syncthreads();
+
+  bool lbad = false;
+  RowStat sd{0.f, 0.0, -1, true};
+  if (v < N && t_ok) {
+    const int p = parents[t0 + v];
+    const int x = tokens[t0 + v];
+    s_par[v] = p;
+    s_tok[v] = x;
+    if (v == 0) lbad |= p != -1;
+    else lbad |= p < 0 || p >= v || x < 0 || x >= V;
+    RowStat st = merge_row(part + (t0 + v) * nchunk, nchunk, c32, greedy);
+    lbad |= !st.ok;
+    s_mt[v] = st.m;
+    s_zt[v] = st.Z;
+    s_idx[v] = st.idx;
+    if (!greedy) {
+      lbad |= !uniform_ok(us[t0 + v]);
+      if (v >= 1) {
+        lbad |= !uniform_ok(ua[t0 + v]);
+        sd = merge_row(part + (L.RT + d0 + v - 1) * nchunk, nchunk, c32, false);
+        lbad |= !sd.ok;
+      }
+    }
+    s_depth[0][v] = v == 0 ? 0 : (1 << 20);
+  }
+  if (lbad) s_bad = 1;
+  __syncthreads();
+  const bool bad0 = s_bad != 0;
+
+  // depths by repeated relaxation (parents precede children)
+  int cur = 0;
+  if (!bad0) {
+    for (int it = 0; it <= max_depth; ++it) {
+      if (v < N) s_depth[cur ^ 1][v] = v == 0 ? 0 : min(s_depth[cur][s_par[v]] + 1, 1 << 20);
+      __syncthreads();
+      cur ^= 1;
+    }
+    if (v < N && s_depth[cur][v] > max_depth) s_bad = 1;
+  }
+  __syncthreads();
+  int32_t* orow = out + (long long)b * width;
+  int32_t* nrow = out_nodes + (long long)b * width;
+  if (s_bad) {
+    for (int k = v; k < width; k += blockDim.x) { orow[k] = -1; nrow[k] = -1; }
+    if (v == 0) { num_acc[b] = -1; jobs[b].kind = JOB_NONE; }
+    return;
+  }
+  const int depth = v < N ? s_depth[cur][v] : 0;
+
+  // acceptance per node against the parent's target row
+  int acc = 0;
+  if (v >= 1 && v < N) {
+    const int p = s_par[v], x = s_tok[v];
+    if (greedy) {
+      acc = x == s_idx[p];
+    } else {
+      RowStat stp{s_mt[p], s_zt[p], -1, true};
+      double pt = prob_at<DT>(tgt, t0 + p, V, x, stp, c32);
+      double pd = prob_at<DT>(dft, d0 + v - 1, V, x, sd, c32);
+      acc = (double)ua[t0 + v] * pd < pt;
+    }
+  }
+  int oc = 0;
+  if (v < N) s_ok[0][v] = v == 0 ? 1 : acc;
+  __syncthreads();
+  for (int it = 0; it < max_depth; ++it) {
+    if (v < N) s_ok[oc ^ 1][v] = v == 0 ? 1 : (acc && s_ok[oc][s_par[v]]);
+    __syncthreads();
+    oc ^= 1;
+  }
+  // end node: deepest kept node, lowest index on ties
+  if (v < N && s_ok[oc][v]) {
+    unsigned long long key = ((unsigned long long)depth << 32) | (unsigned)(0x7fffffff - v);
+    atomicMax(&s_best, key);
+  }
+  __syncthreads();
+  const int e = 0x7fffffff - (int)(unsigned)(s_best & 0xffffffffull);
+  const int de = (int)(s_best >> 32);
+  if (v >= 1 && v < N && s_par[v] == e) atomicMin(&s_child, v);
+  __syncthreads();
+  if (v == 0) {
+    for (int k = 0; k < width; ++k) { orow[k] = -1; nrow[k] = -1; }
+    int w = e;
+    for (int k = de - 1; k >= 0; --k) {
+      orow[k] = s_tok[w];
+      nrow[k] = w;
+      w = s_par[w];
+    }
+    num_acc[b] = de;
+    SampleJob J;
+    J.pos = de;
+    J.pad = 0;
+    J.trow = t0 + e;
+    J.drow = 0;
+    J.rho = 0.0;
+    J.md = 0.0f;
+    J.mt = s_mt[e];
+    if (greedy) {
+      orow[de] = s_idx[e];
+      J.kind = JOB_NONE;
+      J.c64 = 0.0;
+      J.u = 0.0f;
+    } else {
+      J.c64 = c64_of(T);
+      J.u = us[t0 + e];
+      const int c = s_child;
+      if (c == 0x7fffffff) {
+        J.kind = JOB_BONUS;
+      } else {
+        J.kind = JOB_RESIDUAL;
+        J.drow = d0 + c - 1;
+        RowStat sc = merge_row(part + (L.RT + d0 + c - 1) * nchunk, nchunk, c32, false);
+        J.md = sc.m;
+        J.rho = s_zt[e] / sc.Z;
+      }
+    }
+    jobs[b] = J;
+  }
+}
+
+hipError_t launch_accept_tree(int dt, const void* tgt, const void* dft, int V, const Layout& L, int max_depth,
+                              const int32_t* tokens, const int32_t* parents, const float* ua, const float* us,
+                              const float* temperature, const Partial* part, int nchunk, int32_t* out,
+                              int32_t* out_nodes, int32_t* num_acc, SampleJob* jobs, hipStream_t st) {
+  if (L.B == 0) return hipSuccess;
+  int threads = ((L.gamma + 63) / 64) * 64;
+  if (dt == 1)
+    hipLaunchKernelGGL(k_accept_tree<1>, dim3(L.B), dim3(threads), 0, st, tgt, dft, V, L, max_depth, tokens, parents,
+                       ua, us, temperature, part, nchunk, out, out_nodes, num_acc, jobs);
+  else
+    hipLaunchKernelGGL(k_accept_tree<0>, dim3(L.B), dim3(threads), 0, st, tgt, dft, V, L, max_depth, tokens, parents,
+                       ua, us, temperature, part, nchunk, out, out_nodes, num_acc, jobs);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,288 @@
+// api.hip -- C ABI of libspecverify (declared in include/specverify.h).
+//
+// Host side only: validates arguments, carves the caller's workspace and
+// enqueues the kernels on the caller's stream. It never allocates device
+// memory and never synchronises.
+#include "specverify.h"
+#include "sv_internal.h"
+
+#include <stdlib.h>
+
+#include <atomic>
+#include <mutex>
+#include <vector>
+
+using namespace sv;
+
+static_assert(sizeof(Partial) == 16, "Partial layout");
+static_assert(sizeof(TileRec) == 64, "TileRec layout");
+
+namespace {
+
+// Chunk of a row handled by one row-statistics workgroup, in 16-byte vectors
+// (a multiple of kTPB * kU). Fixed per process; SPECVERIFY_CHUNK_VECS overrides it.
+int chunk_vecs() {
+  static std::atomic<int> cached{0};
+  int v = cached.load(std::memory_order_relaxed);
+  if (v) return v;
+  v = 2 * kTPB * kU;
+  if (const char* e = getenv("SPECVERIFY_CHUNK_VECS")) {
+    int x = atoi(e);
+    if (x >= kTPB * kU && x % (kTPB * kU) == 0 && x <= (1 << 22)) v = x;
+  }
+  cached.store(v, std::memory_order_relaxed);
+  return v;
+}
+
+int per_vec(int dt) { return dt == SV_BF16 ? 8 : 4; }
+
+int nchunk_for(int V, int dt) {
+  int nvec = V / per_vec(dt);
+  int cv = chunk_vecs();
+  int n = (nvec + cv - 1) / cv;
+  return n < 1 ? 1 : n;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Carve {
+  size_t part, jobs, recs, total;
+};
+
+Carve carve(long long rows, int B, int V, int dt) {
+  Carve c;
+  const int nchunk = nchunk_for(V, dt);
+  const int ntile = (V + kTile - 1) / kTile;
+  c.part = 0;
+  c.jobs = align256((size_t)rows * nchunk * sizeof(Partial));
+  c.recs = c.jobs + align256((size_t)B * sizeof(SampleJob));
+  c.total = c.recs + align256((size_t)B * ntile * sizeof(TileRec));
+  return c;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+size_t esize(int dt) { return dt == SV_BF16 ? 2 : 4; }
+
+// ---- optional timing of the row-statistics kernel
+struct Timing {
+  bool on = false;
+  std::vector<hipEvent_t> ev;  // pairs
+  int used = 0;
+  static constexpr int kMax = 4096;
+} g_timing;
+std::mutex g_timing_mu;
+
+void timing_mark(hipStream_t st, bool start) {
+  if (!g_timing.on) return;
+  int i = g_timing.used;
+  if (i >= Timing::kMax) return;
+  (void)hipEventRecord(g_timing.ev[2 * i + (start ? 0 : 1)], st);
+  if (!start) g_timing.used = i + 1;
+}
+
+int launch_stats(int dt, const void* tgt, const void* dft, int V, const Layout& L, const float* temperature,
+                 Partial* part, hipStream_t st) {
+  timing_mark(st, true);
+  hipError_t e = launch_row_stats(dt, tgt, dft, V, L, temperature, chunk_vecs(), nchunk_for(V, dt), part, st);
+  timing_mark(st, false);
+  return e == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t dtype) {
+  if (B < 0 || gamma < 0 || gamma > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB || (dtype != 0 && dtype != 1))
+    return 0;
+  return carve((long long)B * (2 * gamma + 1), B, V, dtype).total;
+}
+
+size_t spec_verify_ragged_workspace_bytes(int32_t B, int32_t total_draft, int32_t gamma_max, int32_t V,
+                                          int32_t dtype) {
+  if (B < 0 || total_draft < 0 || gamma_max < 0 || gamma_max > SV_MAX_GAMMA || V < 1 || V > SV_MAX_VOCAB ||
+      (dtype != 0 && dtype != 1))
+    return 0;
+  return carve((long long)2 * total_draft + B, B, V, dtype).total;
+}
+
+size_t spec_verify_tree_workspace_bytes(int32_t B, int32_t N, int32_t V, int32_t dtype) {
+  if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > SV_MAX_VOCAB || (dtype != 0 && dtype != 1)) return 0;
+  return carve((long long)B * (2 * N - 1), B, V, dtype).total;
+}
+
+size_t spec_row_softmax_stats_workspace_bytes(int32_t rows, int32_t V, int32_t dtype) {
+  if (rows < 0 || V < 1 || V > SV_MAX_VOCAB || (dtype != 0 && dtype != 1)) return 0;
+  return align256((size_t)rows * nchunk_for(V, dtype) * sizeof(Partial));
+}
+
+static int check_common(const void* tgt, const void* dft, bool need_dft, int32_t dtype, int32_t V) {
+  if (dtype != SV_F32 && dtype != SV_BF16) return SV_EDTYPE;
+  if (V < 1 || V > SV_MAX_VOCAB) return SV_EINVAL;
+  if (!tgt || (need_dft && !dft)) return SV_EINVAL;
+  if (!aligned(tgt, esize(dtype)) || (need_dft && !aligned(dft, esize(dtype)))) return SV_EALIGN;
+  return SV_OK;
+}
+
+static int check_ws(const void* ws, size_t have, size_t need) {
+  if (need == 0 || !ws || have < need || !aligned(ws, 256)) return SV_ENOWS;
+  return SV_OK;
+}
+
+int spec_verify(const void* target_logits, const void* draft_logits, int32_t dtype, const int32_t* draft_tokens,
+                const float* u_accept, const float* u_sample, const float* temperature, int32_t B, int32_t gamma,
+                int32_t V, int32_t* out_tokens, int32_t* num_accepted, float* diag_probs, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (B < 0 || gamma < 0 || gamma > SV_MAX_GAMMA) return SV_EINVAL;
+  if (B == 0) return SV_OK;
+  int rc = check_common(target_logits, draft_logits, gamma > 0, dtype, V);
+  if (rc) return rc;
+  if (!u_sample || !temperature || !out_tokens || !num_accepted) return SV_EINVAL;
+  if (gamma > 0 && (!draft_tokens || !u_accept)) return SV_EINVAL;
+  const long long RT = (long long)B * (gamma + 1), RD = (long long)B * gamma;
+  Carve cv = carve(RT + RD, B, V, dtype);
+  rc = check_ws(workspace, workspace_bytes, cv.total);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  Partial* part = reinterpret_cast<Partial*>(ws + cv.part);
+  SampleJob* jobs = reinterpret_cast<SampleJob*>(ws + cv.jobs);
+  TileRec* recs = reinterpret_cast<TileRec*>(ws + cv.recs);
+  Layout L{LAYOUT_DENSE, B, gamma, nullptr, 0, RT, RD};
+  if ((rc = launch_stats(dtype, target_logits, draft_logits, V, L, temperature, part, st))) return rc;
+  if (launch_accept_chain(dtype, target_logits, draft_logits, V, L, draft_tokens, u_accept, u_sample, temperature,
+                          part, nchunk_for(V, dtype), out_tokens, gamma + 1, num_accepted, diag_probs, jobs,
+                          st) != hipSuccess)
+    return SV_EHIP;
+  if (launch_sample(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, gamma + 1, st) != hipSuccess)
+    return SV_EHIP;
+  return SV_OK;
+}
+
+int spec_verify_ragged(const void* target_logits, const void* draft_logits, int32_t dtype, const int32_t* cu_gamma,
+                       int32_t total_draft, const int32_t* draft_tokens, const float* u_accept,
+                       const float* u_sample, const float* temperature, int32_t B, int32_t gamma_max, int32_t V,
+                       int32_t* out_tokens, int32_t* num_accepted, float* diag_probs, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (B < 0 || total_draft < 0 || gamma_max < 0 || gamma_max > SV_MAX_GAMMA) return SV_EINVAL;
+  if (B == 0) return SV_OK;
+  if ((long long)total_draft > (long long)B * gamma_max) return SV_EINVAL;
+  int rc = check_common(target_logits, draft_logits, total_draft > 0, dtype, V);
+  if (rc) return rc;
+  if (!cu_gamma || !u_sample || !temperature || !out_tokens || !num_accepted) return SV_EINVAL;
+  if (total_draft > 0 && (!draft_tokens || !u_accept)) return SV_EINVAL;
+  const long long RT = (long long)total_draft + B, RD = total_draft;
+  Carve cv = carve(RT + RD, B, V, dtype);
+  rc = check_ws(workspace, workspace_bytes, cv.total);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  Partial* part = reinterpret_cast<Partial*>(ws + cv.part);
+  SampleJob* jobs = reinterpret_cast<SampleJob*>(ws + cv.jobs);
+  TileRec* recs = reinterpret_cast<TileRec*>(ws + cv.recs);
+  Layout L{LAYOUT_RAGGED, B, gamma_max, cu_gamma, total_draft, RT, RD};
+  if ((rc = launch_stats(dtype, target_logits, draft_logits, V, L, temperature, part, st))) return rc;
+  if (launch_accept_chain(dtype, target_logits, draft_logits, V, L, draft_tokens, u_accept, u_sample, temperature,
+                          part, nchunk_for(V, dtype), out_tokens, gamma_max + 1, num_accepted, diag_probs, jobs,
+                          st) != hipSuccess)
+    return SV_EHIP;
+  if (launch_sample(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, gamma_max + 1, st) !=
+      hipSuccess)
+    return SV_EHIP;
+  return SV_OK;
+}
+
+int spec_verify_tree(const void* target_logits, const void* draft_logits, int32_t dtype, const int32_t* node_tokens,
+                     const int32_t* parents, const float* u_accept, const float* u_sample, const float* temperature,
+                     int32_t B, int32_t N, int32_t V, int32_t max_depth, int32_t* out_tokens, int32_t* out_nodes,
+                     int32_t* num_accepted, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES || max_depth < 0 || max_depth >= N) return SV_EINVAL;
+  if (B == 0) return SV_OK;
+  int rc = check_common(target_logits, draft_logits, N > 1, dtype, V);
+  if (rc) return rc;
+  if (!node_tokens || !parents || !u_accept || !u_sample || !temperature || !out_tokens || !out_nodes ||
+      !num_accepted)
+    return SV_EINVAL;
+  const long long RT = (long long)B * N, RD = (long long)B * (N - 1);
+  Carve cv = carve(RT + RD, B, V, dtype);
+  rc = check_ws(workspace, workspace_bytes, cv.total);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  Partial* part = reinterpret_cast<Partial*>(ws + cv.part);
+  SampleJob* jobs = reinterpret_cast<SampleJob*>(ws + cv.jobs);
+  TileRec* recs = reinterpret_cast<TileRec*>(ws + cv.recs);
+  Layout L{LAYOUT_TREE, B, N, nullptr, 0, RT, RD};
+  if ((rc = launch_stats(dtype, target_logits, draft_logits, V, L, temperature, part, st))) return rc;
+  if (launch_accept_tree(dtype, target_logits, draft_logits, V, L, max_depth, node_tokens, parents, u_accept,
+                         u_sample, temperature, part, nchunk_for(V, dtype), out_tokens, out_nodes, num_accepted,
+                         jobs, st) != hipSuccess)
+    return SV_EHIP;
+  if (launch_sample(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, max_depth + 1, st) !=
+      hipSuccess)
+    return SV_EHIP;
+  return SV_OK;
+}
+
+int spec_row_softmax_stats(const void* logits, int32_t dtype, int32_t rows, int32_t V, const float* temperature,
+                           float* out_max, float* out_logz, int32_t* out_argmax, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (rows < 0) return SV_EINVAL;
+  if (rows == 0) return SV_OK;
+  int rc = check_common(logits, nullptr, false, dtype, V);
+  if (rc) return rc;
+  if (!temperature || !out_max || !out_logz || !out_argmax) return SV_EINVAL;
+  rc = check_ws(workspace, workspace_bytes, spec_row_softmax_stats_workspace_bytes(rows, V, dtype));
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Partial* part = static_cast<Partial*>(workspace);
+  Layout L{LAYOUT_ROWS, rows, 0, nullptr, 0, rows, 0};
+  if ((rc = launch_stats(dtype, logits, nullptr, V, L, temperature, part, st))) return rc;
+  if (launch_stats_finalize(part, nchunk_for(V, dtype), rows, temperature, out_max, out_logz, out_argmax, st) !=
+      hipSuccess)
+    return SV_EHIP;
+  return SV_OK;
+}
+
+const char* spec_verify_strerror(int status) {
+  switch (status) {
+    case SV_OK: return "success";
+    case SV_EINVAL: return "invalid argument (null pointer, size or count out of range)";
+    case SV_EDTYPE: return "unsupported dtype (expected SV_F32 or SV_BF16)";
+    case SV_ENOWS: return "workspace missing, too small or not 256-byte aligned";
+    case SV_EALIGN: return "logits pointer not aligned to its element size";
+    case SV_EHIP: return "HIP runtime or kernel launch failure";
+    default: return "unknown status";
+  }
+}
+
+int spec_verify_version(void) { return 1; }
+
+int spec_verify_timing_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (enable) {
+    if (g_timing.ev.empty()) {
+      g_timing.ev.resize(2 * Timing::kMax);
+      for (auto& e : g_timing.ev)
+        if (hipEventCreate(&e) != hipSuccess) return SV_EHIP;
+    }
+    g_timing.used = 0;
+    g_timing.on = true;
+  } else {
+    g_timing.on = false;
+  }
+  return SV_OK;
+}
+
+int spec_verify_timing_read(float* ms_out, int32_t max, int32_t* count) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (count) *count = g_timing.used;
+  for (int i = 0; i < g_timing.used && i < max; ++i) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]) != hipSuccess) return SV_EHIP;
+    if (ms_out) ms_out[i] = ms;
+  }
+  return SV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,191 @@
+// sv_internal.h -- shared types and device helpers of libspecverify (gfx950).
+//
+// Pipeline of one verify call (all on the caller's stream):
+//   1. row_stats   : one streaming pass over every logit row that the method
+//                    reads -> per (row, chunk) max / sum of 2^{(x-max)c} (T>0)
+//                    or max / lowest argmax (T==0), fp32, 16-byte loads.
+//   2. accept      : per request: merge chunk partials (fp64), acceptance
+//                    test per position / tree node, first rejection, greedy
+//                    outputs, and one sampling job per request.
+//   3. sample_tiles: per (job, tile): fp64 masses of the bonus row or of the
+//                    residual max(0, e_t - rho e_d) against an estimate of
+//                    rho = Z_t / Z_d, plus the few tokens whose side of the
+//                    residual cut the estimate cannot decide.
+//   4. sample_pick : per job: exact rho, tile prefix, inverse-CDF search in
+//                    the selected tile (fp64), token written to out_tokens.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kTPB = 256;        // threads per workgroup (4 waves of 64)
+constexpr int kU = 4;            // 16-byte vectors per thread per step
+constexpr int kTile = 8192;      // elements per sampling tile
+constexpr int kAmbMax = 7;       // undecided residual tokens kept per tile
+constexpr double kLog2e = 1.4426950408889634073599246810019;
+constexpr double kRhoBand = 1e-5;  // relative half-width of the undecided band around rho
+
+// Layout of requests over rows.
+enum LayoutMode : int { LAYOUT_DENSE = 0, LAYOUT_RAGGED = 1, LAYOUT_TREE = 2, LAYOUT_ROWS = 3 };
+
+struct Layout {
+  int mode;
+  int B;
+  int gamma;            // dense gamma, ragged gamma_max, tree N (nodes)
+  const int32_t* cu;    // ragged: cu_gamma [B+1]
+  int total_draft;      // ragged: rows of the draft array
+  long long RT, RD;     // rows of the target and draft arrays
+};
+
+// Partial statistics of one (row, chunk).
+struct Partial {
+  float m;    // chunk maximum (exact value of a logit), -inf if none
+  float s;    // T>0: sum over the chunk of 2^{(x-m)c}; T==0: 0, or NaN if the chunk holds NaN/+inf
+  int idx;    // T==0: lowest index of the maximum (-1 if none)
+  int flag;   // 1 when written
+};
+
+enum JobKind : int { JOB_NONE = 0, JOB_BONUS = 1, JOB_RESIDUAL = 2 };
+
+// One sampling job per request, written by the accept kernels.
+struct SampleJob {
+  int kind;
+  int pos;            // output column of the drawn token
+  long long trow;     // target row (global)
+  long long drow;     // draft row (global, residual only)
+  double c64;         // log2(e) / T
+  double rho;         // estimate of Z_t / Z_d (residual only)
+  float mt, md;       // row maxima (exact)
+  float u;            // sampling uniform
+  int pad;
+};
+
+// Per (job, tile) record of the sampling pass (fp64 sums in ascending tile order).
+struct TileRec {
+  double zt;          // sum of e_t
+  double zd;          // sum of e_d (residual)
+  double dpos;        // sum over decided-positive tokens of (e_t - rho_est e_d)
+  double bpos;        // sum over decided-positive tokens of e_d
+  int namb;           // number of undecided tokens (may exceed kAmbMax)
+  int amb[kAmbMax];   // the first kAmbMax undecided token indices, ascending
+};
+
+// ---------------------------------------------------------------------------
+// Temperature handling shared by every kernel: identical expressions give
+// identical values in every kernel.
+
+__device__ __forceinline__ bool temperature_ok(float T) {
+  // usable: 0 (greedy) or a normal positive finite float
+  return T == 0.0f || (T >= 1.17549435e-38f && T <= 3.40282347e+38f);
+}
+__device__ __forceinline__ float c32_of(float T) { return (float)(kLog2e / (double)T); }
+__device__ __forceinline__ double c64_of(float T) { return kLog2e / (double)T; }
+__device__ __forceinline__ bool uniform_ok(float u) { return u >= 0.0f && u < 1.0f; }  // false for NaN
+
+// ---------------------------------------------------------------------------
+// Element access.
+
+template <int DT> struct Elem;
+template <> struct Elem<0> {  // float32
+  using T = float;
+  static constexpr int kPerVec = 4;
+  __device__ __forceinline__ static float at(const void* p, long long i) {
+    return reinterpret_cast<const float*>(p)[i];
+  }
+};
+template <> struct Elem<1> {  // bfloat16 bit patterns
+  using T = uint16_t;
+  static constexpr int kPerVec = 8;
+  __device__ __forceinline__ static float at(const void* p, long long i) {
+    uint32_t b = (uint32_t)reinterpret_cast<const uint16_t*>(p)[i] << 16;
+    return __uint_as_float(b);
+  }
+};
+
+// Unpack a 16-byte vector into floats.
+template <int DT> __device__ __forceinline__ void unpack(const uint4& w, float* x);
+template <> __device__ __forceinline__ void unpack<0>(const uint4& w, float* x) {
+  x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y);
+  x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+}
+template <> __device__ __forceinline__ void unpack<1>(const uint4& w, float* x) {
+  x[0] = __uint_as_float(w.x << 16); x[1] = __uint_as_float(w.x & 0xffff0000u);
+  x[2] = __uint_as_float(w.y << 16); x[3] = __uint_as_float(w.y & 0xffff0000u);
+  x[4] = __uint_as_float(w.z << 16); x[5] = __uint_as_float(w.z & 0xffff0000u);
+  x[6] = __uint_as_float(w.w << 16); x[7] = __uint_as_float(w.w & 0xffff0000u);
+}
+
+// Vector split of one row: `head` scalar elements until a 16-byte boundary,
+// `nvec` full vectors, then `tail` scalar elements.
+struct RowSplit {
+  int head, nvec, tail;
+};
+template <int DT>
+__device__ __forceinline__ RowSplit split_row(const void* row, int V) {
+  constexpr int es = sizeof(typename Elem<DT>::T);
+  constexpr int epv = Elem<DT>::kPerVec;
+  uintptr_t a = reinterpret_cast<uintptr_t>(row);
+  int head = (int)(((16u - (unsigned)(a & 15u)) & 15u) / es);
+  if (head > V) head = V;
+  int nvec = (V - head) / epv;
+  return RowSplit{head, nvec, V - head - nvec * epv};
+}
+
+// ---------------------------------------------------------------------------
+// 2^a in double precision for a <= 0 (NaN propagates): a = n + f with
+// n = rint(a), |f| <= 1/2, and 2^f = exp(f ln 2) by its Taylor series to
+// degree 13 (coefficients ln2^k / k!, truncation below 5e-18 relative).
+__device__ __forceinline__ double exp2_f64(double a) {
+  if (!(a >= -1100.0)) return (a != a) ? a : 0.0;
+  double n = __builtin_rint(a);
+  double f = a - n;
+  double p = 0x1.816193166d0f9p-40;
+  p = __builtin_fma(p, f, 0x1.c3bd650fc2986p-36);
+  p = __builtin_fma(p, f, 0x1.e8cac7351bb25p-32);
+  p = __builtin_fma(p, f, 0x1.e4cf5158b8ecap-28);
+  p = __builtin_fma(p, f, 0x1.b5253d395e7c4p-24);
+  p = __builtin_fma(p, f, 0x1.62c0223a5c824p-20);
+  p = __builtin_fma(p, f, 0x1.ffcbfc588b0c7p-17);
+  p = __builtin_fma(p, f, 0x1.430912f86c787p-13);
+  p = __builtin_fma(p, f, 0x1.5d87fe78a6731p-10);
+  p = __builtin_fma(p, f, 0x1.3b2ab6fba4e77p-7);
+  p = __builtin_fma(p, f, 0x1.c6b08d704a0c0p-5);
+  p = __builtin_fma(p, f, 0x1.ebfbdff82c58fp-3);
+  p = __builtin_fma(p, f, 0x1.62e42fefa39efp-1);
+  p = __builtin_fma(p, f, 1.0);
+  return __builtin_ldexp(p, (int)n);
+}
+
+// fp32 2^x on the hardware transcendental unit (v_exp_f32).
+__device__ __forceinline__ float exp2_f32(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Wave64 / workgroup reductions.
+
+template <typename T, typename F>
+__device__ __forceinline__ T wave_reduce(T v, F op) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = op(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Host-side launchers (defined next to their kernels).
+hipError_t launch_row_stats(int dt, const void* tgt, const void* dft, int V, const Layout& L,
+                            const float* temperature, int chunk_vecs, int nchunk, Partial* part,
+                            hipStream_t st);
+hipError_t launch_accept_chain(int dt, const void* tgt, const void* dft, int V, const Layout& L,
+                               const int32_t* tokens, const float* ua, const float* us, const float* temperature,
+                               const Partial* part, int nchunk, int32_t* out, int out_width, int32_t* num_acc,
+                               float* diag, SampleJob* jobs, hipStream_t st);
+hipError_t launch_accept_tree(int dt, const void* tgt, const void* dft, int V, const Layout& L, int max_depth,
+                              const int32_t* tokens, const int32_t* parents, const float* ua, const float* us,
+                              const float* temperature, const Partial* part, int nchunk, int32_t* out,
+                              int32_t* out_nodes, int32_t* num_acc, SampleJob* jobs, hipStream_t st);
+hipError_t launch_sample(int dt, const void* tgt, const void* dft, int V, int B, const SampleJob* jobs,
+                         TileRec* recs, int32_t* out, int out_width, hipStream_t st);
+hipError_t launch_stats_finalize(const Partial* part, int nchunk, int rows, const float* temperature,
+                                 float* out_max, float* out_logz, int32_t* out_argmax, hipStream_t st);
+
+}  // namespace sv

@@ -178,5 +178,7 @@ def test_ragged_cu_validation():
     cu[3] = cu[4] + 1  # request 2 would own a negative count, request 3 too many
     r = oracle.verify_chain(d["target"], d["draft"], d["draft_tokens"], d["u_accept"], d["u_sample"],
                             d["temperature"], gamma=d["gamma_max"], cu_gamma=cu)
-    assert r["num_accepted"][3] == -1
-    assert r["num_accepted"][0] >= 0
+    assert (r["num_accepted"] == -1).all()  # a malformed layout fails the whole batch
+    ok = oracle.verify_chain(d["target"], d["draft"], d["draft_tokens"], d["u_accept"], d["u_sample"],
+                             d["temperature"], gamma=d["gamma_max"], cu_gamma=d["cu_gamma"])
+    assert (ok["num_accepted"] >= 0).all()
