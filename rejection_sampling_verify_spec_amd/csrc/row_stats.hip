@@ -14,7 +14,9 @@
 // K = fl(m c) an exact fp32 number, so every term of the group shares one
 // exactly known offset; the thread statistic is converted to the offset m c
 // once at the end with the exact remainder r = m c - K (error-free product).
-// When |m c| overflows fp32 the chunk is recomputed with (x - m) c.
+// The remainder is at most half an ulp of K, so the trick needs |K| < 2^22
+// (then |r| <= 1/4 and no term can overflow); a chunk where some |m c| is
+// larger (tiny temperatures, huge logits) is recomputed with (x - m) c.
 #include "sv_internal.h"
 
 #include <float.h>
@@ -72,7 +74,7 @@ __device__ __forceinline__ void group_update(float& m, float& K, float& s, bool&
   for (int i = 1; i < N; ++i) gm = fmaxf(gm, x[i]);
   float mn = fmaxf(m, gm);
   float Kn = mn == -INFINITY ? 0.0f : mn * c;
-  ovf |= !(fabsf(Kn) <= FLT_MAX);
+  ovf |= !(fabsf(Kn) <= 0x1p22f);  // also catches +inf maxima
   float f = m == -INFINITY ? 0.0f : exp2_f32(K - Kn);
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
@@ -145,7 +147,7 @@ __device__ void stats_sampling(const void* rowp, const RowSplit& sp, int v0, int
     if (tid == 0) *out = Partial{m, s, -1, 1};
     return;
   }
-  // Rare path: |max * c| beyond fp32 range. Exact maximum first, then sum 2^{(x-M)c}.
+  // Rare path: |max * c| >= 2^22 somewhere in the chunk. Exact maximum first, then sum 2^{(x-M)c}.
   float mm = m;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
@@ -229,7 +231,8 @@ __device__ void stats_greedy(const void* rowp, const RowSplit& sp, int v0, int v
   auto scalar = [&](long long j) {
     float x1 = E::at(rowp, j);
     nan_seen |= x1 != x1;
-    if (x1 > m) { m = x1; idx = (int)j; }
+    // head elements precede every vector element: a tie goes to the lower index
+    if (x1 > m || (x1 == m && (unsigned)j < (unsigned)idx)) { m = x1; idx = (int)j; }
   };
   if (do_head && tid < sp.head) scalar(tid);
   if (do_tail && tid < sp.tail) scalar((long long)sp.head + (long long)sp.nvec * EPV + tid);

@@ -122,6 +122,17 @@ def test_greedy_ties(sv):
     d["target"] = bits
     d["draft"] = np.zeros((B, g, V), np.uint16)
     check_chain(sv, d, "greedy ties bf16")
+    # odd V: rows start off 16-byte boundaries, so ties span head, vector and tail elements
+    V2 = 4099
+    t2 = rng.integers(-1, 2, size=(B, g + 1, V2)).astype(np.float32)
+    t2[:, :, :3] = 1.0
+    t2[:, :, V2 - 2:] = 1.0
+    a2 = t2.argmax(-1)
+    d2 = dict(target=(t2.view(np.uint32) >> 16).astype(np.uint16), draft=np.zeros((B, g, V2), np.uint16),
+              draft_tokens=a2[:, :g].astype(np.int32), u_accept=np.zeros((B, g), np.float32),
+              u_sample=np.zeros((B, g + 1), np.float32), temperature=np.zeros(B, np.float32))
+    d2["draft_tokens"][::2, 2] = 5
+    check_chain(sv, d2, "greedy ties misaligned bf16")
 
 
 def test_row_softmax_stats(sv):
