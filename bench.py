@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Benchmark of the batched speculative-decoding verify step on one MI355X.
+
+A step is one full verify call (row statistics -> acceptance scan -> residual /
+bonus sampling) over one synthetic batch already resident in HBM. Default
+workload: B=256 requests, gamma=5 drafted tokens, V=128256, bf16 logits
+(target 2.5 * Student-t(3), draft = target + N(0, 1), T = 1).
+
+Prints ONE JSON line: verified draft positions/s, logits GB/s against the
+MI355X HBM peak (formula bytes B*(2g+1)*V*s + B*V*s per step), the roofline
+entry of the dominant kernel (row statistics; durations from HIP events
+recorded on the launch stream), and the CPU oracle timed on the host cores.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large]
+  python bench.py --copy-calibration          # plain copy kernel of known size (PMC scale)
+  python bench.py --summarize-rocprof DIR     # text summary of rocprofv3 output in DIR
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft positions/s + logits HBM GB/s (% of peak), B=256 γ=5 V=128256"
+HBM_PEAK_GBPS = 8000.0
+KERNEL = "k_row_stats"
+PMC_FILE = os.path.join(ROOT, "profiles", "row_stats_large_pmc.json")
+KERNEL_SOURCES = ["rejection_sampling_verify_spec_amd/csrc/row_stats.hip",
+                  "rejection_sampling_verify_spec_amd/csrc/sv_internal.h"]
+
+WORKLOAD_TEXT = {
+    "large": "large-vocab chain verify: B=256, gamma=5, V=128256, bf16 logits, target 2.5*Student-t(3), "
+             "draft = target + N(0,1), T=1.0",
+    "tiny": "tiny chain verify: B=8, gamma=4, V=256, fp32",
+    "mid": "mid chain verify: B=64, gamma=5, V=32000, fp32, 20 spikes +8, T=0.8",
+    "tree": "token-tree verify: B=32, 64 nodes, V=152064, bf16",
+    "ragged": "ragged mixed verify: B=1024, gamma_b in 1..8, V=151936, bf16, 256 greedy",
+}
+
+
+def device_inputs(d, dev):
+    """Generator arrays to device tensors (bf16 bit patterns become torch.bfloat16)."""
+    import numpy as np
+    import torch
+    out = {}
+    for k, a in d.items():
+        if not isinstance(a, np.ndarray):
+            continue
+        if a.dtype == np.uint16:
+            out[k] = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            out[k] = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    return out
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def host_cores() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def workload_accounting(name, d):
+    """(positions, formula bytes, row-statistics algorithmic bytes) per step."""
+    import numpy as np
+    es = 4 if d["target"].dtype == np.float32 else 2
+    V = d["target"].shape[-1]
+    T = d["temperature"]
+    B = T.shape[0]
+    if name == "tree":
+        N = d["target"].shape[1]
+        positions = B * (N - 1)
+        formula = B * (2 * N - 1) * V * es + B * V * es
+        rows_read = B * N + int((T > 0).sum()) * (N - 1)
+    elif name == "ragged":
+        g = np.diff(d["cu_gamma"]).astype(np.int64)
+        positions = int(g.sum())
+        formula = int((2 * g + 1).sum()) * V * es + B * V * es
+        rows_read = int((g + 1).sum() + g[T > 0].sum())
+    else:
+        g = d["draft_tokens"].shape[1]
+        positions = B * g
+        formula = B * (2 * g + 1) * V * es + B * V * es
+        rows_read = B * (g + 1) + int((T > 0).sum()) * g
+    return positions, formula, rows_read * V * es
+
+
+def make_call(sv, name, t, d):
+    """Closure running one verify step on device tensors t."""
+    if name == "tree":
+        return lambda tt: sv.verify_tree(tt["target"], tt["draft"], tt["node_tokens"], tt["parents"],
+                                         tt["u_accept"], tt["u_sample"], tt["temperature"], d["max_depth"])
+    if name == "ragged":
+        return lambda tt: sv.verify_ragged(tt["target"], tt["draft"], tt["cu_gamma"], d["total_draft"],
+                                           tt["draft_tokens"], tt["u_accept"], tt["u_sample"], tt["temperature"],
+                                           d["gamma_max"])
+    return lambda tt: sv.verify_chain(tt["target"], tt["draft"], tt["draft_tokens"], tt["u_accept"],
+                                      tt["u_sample"], tt["temperature"])
+
+
+def oracle_call(name, d, nthreads):
+    import oracle
+    if name == "tree":
+        return oracle.verify_tree(d["target"], d["draft"], d["node_tokens"], d["parents"], d["u_accept"],
+                                  d["u_sample"], d["temperature"], d["max_depth"], nthreads=nthreads)
+    if name == "ragged":
+        return oracle.verify_chain(d["target"], d["draft"], d["draft_tokens"], d["u_accept"], d["u_sample"],
+                                   d["temperature"], gamma=d["gamma_max"], cu_gamma=d["cu_gamma"], nthreads=nthreads)
+    return oracle.verify_chain(d["target"], d["draft"], d["draft_tokens"], d["u_accept"], d["u_sample"],
+                               d["temperature"], nthreads=nthreads)
+
+
+def load_traffic(algo_bytes):
+    """HBM bytes per launch from committed PMC counters, if they match the current kernel source."""
+    if not os.path.exists(PMC_FILE):
+        return None
+    with open(PMC_FILE) as f:
+        pmc = json.load(f)
+    if pmc.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return pmc.get("hbm_bytes_per_launch")
+
+
+def run_bench(args):
+    import numpy as np
+    import torch
+
+    import inputgen
+    import rejection_sampling_verify_spec_amd as sv
+
+    name = args.workload
+    t0 = time.time()
+    d = inputgen.make(name)
+    print(f"bench: generated {name} inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    copies = [device_inputs(d, dev) for _ in range(args.copies)]
+    call = make_call(sv, name, copies[0], d)
+    positions, formula_bytes, k1_bytes = workload_accounting(name, d)
+
+    for i in range(args.warmup):
+        call(copies[i % len(copies)])
+    torch.cuda.synchronize()
+
+    sv.spec_verify_timing_enable(True)
+    torch.cuda.synchronize()
+    start = time.perf_counter()
+    outs = None
+    for i in range(args.steps):
+        outs = call(copies[i % len(copies)])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - start
+    k1_ms = sv.spec_verify_timing_read(args.steps)
+    sv.spec_verify_timing_enable(False)
+    print(f"bench: {args.steps} steps in {elapsed * 1e3:.2f} ms", file=sys.stderr, flush=True)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = positions * args.steps / elapsed
+    gbps = formula_bytes * args.steps / elapsed / 1e9
+    k1_avg_ms = float(np.mean(k1_ms)) if k1_ms else float("nan")
+    k1_gbps = k1_bytes / (k1_avg_ms * 1e-3) / 1e9
+
+    # CPU oracle on the host cores: the same batch (bounded: one verify step of the workload)
+    cores = host_cores()
+    tc = time.perf_counter()
+    ref = oracle_call(name, d, cores)
+    cpu_s = time.perf_counter() - tc
+    na = outs[-1].cpu().numpy()
+    out_tok = outs[0].cpu().numpy()
+    parity_ok = bool(np.array_equal(na, ref["num_accepted"]) and np.array_equal(out_tok, ref["out_tokens"]))
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "verified draft positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "input_dtype": "bf16" if d["target"].dtype == np.uint16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[name], "B": int(d["temperature"].shape[0]),
+                   "V": int(d["target"].shape[-1]), "positions_per_step": positions,
+                   "input_copies_rotated": args.copies},
+        "logits_gbps_formula": round(gbps, 1),
+        "hbm_peak_frac_formula": round(gbps / HBM_PEAK_GBPS, 4),
+        "formula_bytes_per_step": formula_bytes,
+        "roofline": {
+            "bound": "hbm",
+            "kernel": KERNEL,
+            "achieved": round(k1_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(k1_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic(k1_bytes),
+            "algorithmic_bytes_per_launch": k1_bytes,
+            "avg_launch_ms": round(k1_avg_ms, 5),
+            "launches_timed": len(k1_ms),
+        },
+        "cpu_baseline": {
+            "value": round(positions / cpu_s, 1),
+            "unit": "verified draft positions/s",
+            "cores": cores,
+            "kind": "oracle",
+            "sample": f"one full verify step of the same workload ({positions} positions), fp64 oracle, "
+                      f"{cores} threads, {cpu_s:.2f} s wall",
+        },
+        "mean_num_accepted": round(float(np.mean(na[na >= 0])), 4),
+        "parity_vs_oracle": parity_ok,
+    }
+    print(json.dumps(line), flush=True)
+    return 0 if parity_ok else 1
+
+
+def copy_calibration(args):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n,
+                      "launches": args.steps}), flush=True)
+    return 0
+
+
+def summarize_rocprof(path):
+    """Summarise rocprofv3 output found under `path`: kernel stats (avg duration) and, when present,
+    per-dispatch FETCH_SIZE / WRITE_SIZE averages per kernel."""
+    stats = glob.glob(os.path.join(path, "**", "*kernel_stats.csv"), recursive=True)
+    ctrs = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    for p in stats:
+        print(f"# kernel stats: {os.path.relpath(p, path)}")
+        with open(p) as f:
+            rows = list(csv.DictReader(f))
+        print("| kernel | calls | avg ns | min ns | max ns | total % |")
+        print("|---|---|---|---|---|---|")
+        for r in rows:
+            nm = r.get("Name", "")
+            short = nm.split("(")[0][:70]
+            print(f"| {short} | {r.get('Calls')} | {r.get('AverageNs')} | {r.get('MinNs')} | {r.get('MaxNs')} | "
+                  f"{float(r.get('Percentage', 0)):.2f} |")
+    for p in ctrs:
+        print(f"# counters: {os.path.relpath(p, path)}")
+        agg = {}
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                key = (r.get("Kernel_Name", "").split("(")[0][:70], r.get("Counter_Name"))
+                agg.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
+        print("| kernel | counter | dispatches | avg per dispatch |")
+        print("|---|---|---|---|")
+        for (k, c), v in sorted(agg.items()):
+            print(f"| {k} | {c} | {len(v)} | {sum(v) / len(v):.1f} |")
+    return 0
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="large", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize-rocprof", metavar="DIR")
+    args = ap.parse_args()
+    if args.summarize_rocprof:
+        return summarize_rocprof(args.summarize_rocprof)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: only one GPU is measured here; the verify step shards over requests with no "
+              "communication, so N GPUs each run this same single-GPU step. Run with --gpus 1.", file=sys.stderr)
+        return 2
+    if args.copy_calibration:
+        return copy_calibration(args)
+    return run_bench(args)
+
+
+if __name__ == "__main__":
+    sys.exit(main())

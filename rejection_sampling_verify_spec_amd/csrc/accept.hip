@@ -89,23 +89,31 @@ __global__ __launch_bounds__(64) void k_accept_chain(const void* __restrict__ tg
   const bool greedy = T == 0.0f;
   const float c32 = bad || greedy ? 0.0f : c32_of(T);
 
-  // --- pass A: validation and acceptance decisions
+  // --- pass A: validation and acceptance decisions. The lane holding the final
+  // position n (first rejection, or gamma) writes the sampling job from its statistics.
   int n = g;  // first rejected position
+  bool found = false;
   for (int base = 0; base <= g && !bad; base += 64) {
     const int i = base + lane;
     bool lbad = false, reject = false;
+    RowStat st{0.f, 0.0, -1, true}, sd{0.f, 0.0, -1, true};
     if (i <= g) {
-      RowStat st = merge_row(part + (t0 + i) * nchunk, nchunk, c32, greedy);
-      lbad |= !st.ok;
-      if (!greedy) lbad |= !uniform_ok(us[t0 + i]);
+      int x = 0;
+      float u = 0.f, usv = 0.f;
       if (i < g) {
-        const int x = tokens[d0 + i];
+        x = tokens[d0 + i];
+        if (!greedy) u = ua[d0 + i];
+      }
+      if (!greedy) usv = us[t0 + i];
+      st = merge_row(part + (t0 + i) * nchunk, nchunk, c32, greedy);
+      lbad |= !st.ok;
+      if (!greedy) lbad |= !uniform_ok(usv);
+      if (i < g) {
         lbad |= x < 0 || x >= V;
         if (greedy) {
           reject = x != st.idx;
         } else {
-          RowStat sd = merge_row(part + (L.RT + d0 + i) * nchunk, nchunk, c32, false);
-          const float u = ua[d0 + i];
+          sd = merge_row(part + (L.RT + d0 + i) * nchunk, nchunk, c32, false);
           lbad |= !sd.ok || !uniform_ok(u);
           if (!lbad) {
             double pt = prob_at<DT>(tgt, t0 + i, V, x, st, c32);
@@ -119,8 +127,50 @@ __global__ __launch_bounds__(64) void k_accept_chain(const void* __restrict__ tg
       if (greedy) s_amax[i] = st.idx;
     }
     bad = __any(lbad) || bad;
-    unsigned long long rm = __ballot(reject && i < g);
-    if (rm && n == g) n = min(g, base + __builtin_ctzll(rm));
+    const unsigned long long rm = __ballot(reject && i < g);
+    if (!found && rm) {
+      n = base + __builtin_ctzll(rm);
+      found = true;
+    }
+    // job of a sampling request, written by the lane of position n
+    if (!greedy && i == n && (found || i == g)) {
+      SampleJob J;
+      J.kind = n < g ? JOB_RESIDUAL : JOB_BONUS;
+      J.pos = n;
+      J.trow = t0 + n;
+      J.drow = d0 + n;
+      J.c64 = c64_of(T);
+      J.u = us[t0 + n];
+      J.mt = st.m;
+      J.md = n < g ? sd.m : 0.0f;
+      J.rho = n < g ? st.Z / sd.Z : 0.0;
+      J.pad = 0;
+      jobs[b] = J;
+    }
+    if (found) break;
+  }
+  // validation covers every position, also those after the first rejection
+  for (int base = (n / 64 + 1) * 64; base <= g && !bad; base += 64) {
+    const int i = base + lane;
+    bool lbad = false;
+    if (i <= g) {
+      RowStat st = merge_row(part + (t0 + i) * nchunk, nchunk, c32, greedy);
+      lbad |= !st.ok;
+      if (!greedy) lbad |= !uniform_ok(us[t0 + i]);
+      if (i < g) {
+        const int x = tokens[d0 + i];
+        lbad |= x < 0 || x >= V;
+        if (!greedy) {
+          RowStat sd = merge_row(part + (L.RT + d0 + i) * nchunk, nchunk, c32, false);
+          lbad |= !sd.ok || !uniform_ok(ua[d0 + i]);
+          if (!lbad) {  // per-position probabilities for the diagnostics output
+            s_pt[i] = (float)prob_at<DT>(tgt, t0 + i, V, x, st, c32);
+            s_pd[i] = (float)prob_at<DT>(dft, d0 + i, V, x, sd, c32);
+          }
+        }
+      }
+    }
+    bad = __any(lbad) || bad;
   }
   __syncthreads();
 
@@ -147,26 +197,7 @@ __global__ __launch_bounds__(64) void k_accept_chain(const void* __restrict__ tg
     }
   if (lane == 0) {
     num_acc[b] = n;
-    SampleJob J;
-    J.kind = greedy ? JOB_NONE : (n < g ? JOB_RESIDUAL : JOB_BONUS);
-    J.pos = n;
-    J.trow = t0 + n;
-    J.drow = d0 + n;
-    J.c64 = greedy ? 0.0 : c64_of(T);
-    J.u = greedy ? 0.0f : us[t0 + n];
-    J.rho = 0.0;
-    J.mt = J.md = 0.0f;
-    J.pad = 0;
-    if (!greedy) {
-      RowStat st = merge_row(part + (t0 + n) * nchunk, nchunk, c32, false);
-      J.mt = st.m;
-      if (n < g) {
-        RowStat sd = merge_row(part + (L.RT + d0 + n) * nchunk, nchunk, c32, false);
-        J.md = sd.m;
-        J.rho = st.Z / sd.Z;
-      }
-    }
-    jobs[b] = J;
+    if (greedy) jobs[b].kind = JOB_NONE;
   }
 }
 

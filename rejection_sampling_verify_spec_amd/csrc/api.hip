@@ -15,7 +15,7 @@
 using namespace sv;
 
 static_assert(sizeof(Partial) == 16, "Partial layout");
-static_assert(sizeof(TileRec) == 64, "TileRec layout");
+static_assert(sizeof(TileRec) == 128, "TileRec layout");
 
 namespace {
 
@@ -45,6 +45,7 @@ int nchunk_for(int V, int dt) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workspace layout: row-chunk partials | sampling jobs | tile records.
 struct Carve {
   size_t part, jobs, recs, total;
 };
@@ -52,12 +53,20 @@ struct Carve {
 Carve carve(long long rows, int B, int V, int dt) {
   Carve c;
   const int nchunk = nchunk_for(V, dt);
-  const int ntile = (V + kTile - 1) / kTile;
+  const int ntile = (V + kSTile - 1) / kSTile;
   c.part = 0;
   c.jobs = align256((size_t)rows * nchunk * sizeof(Partial));
   c.recs = c.jobs + align256((size_t)B * sizeof(SampleJob));
   c.total = c.recs + align256((size_t)B * ntile * sizeof(TileRec));
   return c;
+}
+
+// SPECVERIFY_FORCE_EXACT_RESIDUAL=1 recomputes every residual tile token by
+// token instead of using the fp32 estimate of Z_t/Z_d (same results; slower).
+// Read on every call so tests can cover that path in-process.
+int force_exact_residual() {
+  const char* e = getenv("SPECVERIFY_FORCE_EXACT_RESIDUAL");
+  return e && e[0] == '1';
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -154,7 +163,7 @@ int spec_verify(const void* target_logits, const void* draft_logits, int32_t dty
                           part, nchunk_for(V, dtype), out_tokens, gamma + 1, num_accepted, diag_probs, jobs,
                           st) != hipSuccess)
     return SV_EHIP;
-  if (launch_sample(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, gamma + 1, st) != hipSuccess)
+  if (launch_sample(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, gamma + 1, force_exact_residual(), st) != hipSuccess)
     return SV_EHIP;
   return SV_OK;
 }
@@ -186,7 +195,7 @@ int spec_verify_ragged(const void* target_logits, const void* draft_logits, int3
                           part, nchunk_for(V, dtype), out_tokens, gamma_max + 1, num_accepted, diag_probs, jobs,
                           st) != hipSuccess)
     return SV_EHIP;
-  if (launch_sample(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, gamma_max + 1, st) !=
+  if (launch_sample(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, gamma_max + 1, force_exact_residual(), st) !=
       hipSuccess)
     return SV_EHIP;
   return SV_OK;
@@ -218,7 +227,7 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int32_
                          u_sample, temperature, part, nchunk_for(V, dtype), out_tokens, out_nodes, num_accepted,
                          jobs, st) != hipSuccess)
     return SV_EHIP;
-  if (launch_sample(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, max_depth + 1, st) !=
+  if (launch_sample(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, max_depth + 1, force_exact_residual(), st) !=
       hipSuccess)
     return SV_EHIP;
   return SV_OK;

@@ -55,14 +55,47 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2,
   m = M;
 }
 
+// Logits are read exactly once here: nontemporal 16-byte loads (streaming
+// hint) measured ~10% faster than plain loads for this pass on MI355X.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// A full group: kU unpredicated 16-byte loads per thread (every index < v1).
+__device__ __forceinline__ void load_group_full(const uint4* vp, int vb, int tid, uint4* w) {
+#pragma unroll
+  for (int u = 0; u < kU; ++u) w[u] = stream_load(vp + vb + u * kTPB + tid);
+}
+
+// The last, partial group of a chunk: out-of-range vectors read a valid
+// address and are replaced by -inf (they add nothing to max or sum).
 template <int DT>
-__device__ __forceinline__ void load_group(const uint4* vp, int vb, int v1, int tid, uint4* w) {
-  const uint4 neg_inf = DT == 1 ? make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u)
-                                : make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
+__device__ __forceinline__ void load_group_tail(const uint4* vp, int vb, int v1, int tid, uint4* w) {
+  const uint32_t ni = DT == 1 ? 0xff80ff80u : 0xff800000u;
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     int v = vb + u * kTPB + tid;
-    w[u] = v < v1 ? vp[v] : neg_inf;
+    uint4 t = stream_load(vp + min(v, v1 - 1));
+    bool in = v < v1;
+    w[u] = make_uint4(in ? t.x : ni, in ? t.y : ni, in ? t.z : ni, in ? t.w : ni);
+  }
+}
+
+// Visit the 16-byte vectors [v0, v1) of a chunk in groups; f(w, vb) gets each group.
+template <int DT, typename F>
+__device__ __forceinline__ void for_each_group(const uint4* vp, int v0, int v1, int tid, F f) {
+  int vb = v0;
+  for (; vb + kU * kTPB <= v1; vb += kU * kTPB) {
+    uint4 w[kU];
+    load_group_full(vp, vb, tid, w);
+    f(w, vb);
+  }
+  if (vb < v1) {
+    uint4 w[kU];
+    load_group_tail<DT>(vp, vb, v1, tid, w);
+    f(w, vb);
   }
 }
 
@@ -116,14 +149,12 @@ __device__ void stats_sampling(const void* rowp, const RowSplit& sp, int v0, int
                                                    (size_t)sp.head * sizeof(typename E::T));
   float m = -INFINITY, K = 0.f, s = 0.f;
   bool ovf = false;
-  for (int vb = v0; vb < v1; vb += kTPB * kU) {
-    uint4 w[kU];
-    load_group<DT>(vp, vb, v1, tid, w);
+  for_each_group<DT>(vp, v0, v1, tid, [&](const uint4* w, int) {
     float x[G];
 #pragma unroll
     for (int u = 0; u < kU; ++u) unpack<DT>(w[u], x + u * EPV);
     group_update<G>(m, K, s, ovf, x, c);
-  }
+  });
   if (do_head && tid < sp.head) {
     float x1 = E::at(rowp, tid);
     group_update<1>(m, K, s, ovf, &x1, c);
@@ -157,15 +188,13 @@ __device__ void stats_sampling(const void* rowp, const RowSplit& sp, int v0, int
   float M = sm[0];
   for (int w = 1; w < kTPB / 64; ++w) M = fmaxf(M, sm[w]);
   float acc = 0.f;
-  for (int vb = v0; vb < v1; vb += kTPB * kU) {
-    uint4 w[kU];
-    load_group<DT>(vp, vb, v1, tid, w);
+  for_each_group<DT>(vp, v0, v1, tid, [&](const uint4* w, int) {
     float x[G];
 #pragma unroll
     for (int u = 0; u < kU; ++u) unpack<DT>(w[u], x + u * EPV);
 #pragma unroll
     for (int i = 0; i < G; ++i) acc += exp2_f32((x[i] - M) * c);
-  }
+  });
   if (do_head && tid < sp.head) acc += exp2_f32((E::at(rowp, tid) - M) * c);
   if (do_tail && tid < sp.tail)
     acc += exp2_f32((E::at(rowp, (long long)sp.head + (long long)sp.nvec * EPV + tid) - M) * c);
@@ -197,9 +226,7 @@ __device__ void stats_greedy(const void* rowp, const RowSplit& sp, int v0, int v
   bool nan_seen = false;
   us2_t mag2 = {0, 0};
   uint32_t mag = 0;
-  for (int vb = v0; vb < v1; vb += kTPB * kU) {
-    uint4 w[kU];
-    load_group<DT>(vp, vb, v1, tid, w);
+  for_each_group<DT>(vp, v0, v1, tid, [&](const uint4* w, int vb) {
     float x[G];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -227,7 +254,7 @@ __device__ void stats_greedy(const void* rowp, const RowSplit& sp, int v0, int v
       m = gm;
       idx = gi;
     }
-  }
+  });
   auto scalar = [&](long long j) {
     float x1 = E::at(rowp, j);
     nan_seen |= x1 != x1;

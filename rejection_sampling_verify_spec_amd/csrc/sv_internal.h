@@ -7,12 +7,11 @@
 //   2. accept      : per request: merge chunk partials (fp64), acceptance
 //                    test per position / tree node, first rejection, greedy
 //                    outputs, and one sampling job per request.
-//   3. sample_tiles: per (job, tile): fp64 masses of the bonus row or of the
-//                    residual max(0, e_t - rho e_d) against an estimate of
-//                    rho = Z_t / Z_d, plus the few tokens whose side of the
-//                    residual cut the estimate cannot decide.
-//   4. sample_pick : per job: exact rho, tile prefix, inverse-CDF search in
-//                    the selected tile (fp64), token written to out_tokens.
+//   3. sample_tiles: per (job, tile of kSTile tokens): fp64 masses of the bonus
+//                    row or of the residual max(0, e_t - rho e_d) against an
+//                    estimate of rho = Z_t / Z_d.
+//   4. sample_pick : per job: exact rho, tile prefix, inverse-CDF search in the
+//                    selected tile (fp64), token written to out_tokens.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,8 +21,8 @@ namespace sv {
 
 constexpr int kTPB = 256;        // threads per workgroup (4 waves of 64)
 constexpr int kU = 4;            // 16-byte vectors per thread per step
-constexpr int kTile = 8192;      // elements per sampling tile
-constexpr int kAmbMax = 7;       // undecided residual tokens kept per tile
+constexpr int kSTile = 2048;     // tokens per sampling tile (8 per thread)
+constexpr int kGrp = 5;          // groups of undecided residual tokens kept per tile
 constexpr double kLog2e = 1.4426950408889634073599246810019;
 constexpr double kRhoBand = 1e-5;  // relative half-width of the undecided band around rho
 
@@ -62,14 +61,20 @@ struct SampleJob {
   int pad;
 };
 
-// Per (job, tile) record of the sampling pass (fp64 sums in ascending tile order).
+// Per (job, tile) record of the sampling pass (fp64 sums in a fixed order).
+// Undecided tokens (likelihood ratio inside the band around rho~) are kept
+// as groups of equal logit difference l_t - l_d: a group shares one ratio,
+// hence one residual sign, and contributes max(0, sum e_t - rho sum e_d).
 struct TileRec {
   double zt;          // sum of e_t
-  double zd;          // sum of e_d (residual)
-  double dpos;        // sum over decided-positive tokens of (e_t - rho_est e_d)
+  double zd;          // sum of e_d (residual); the exact tile mass once the pick has run
+  double dpos;        // sum over decided-positive tokens of (e_t - rho~ e_d)
   double bpos;        // sum over decided-positive tokens of e_d
-  int namb;           // number of undecided tokens (may exceed kAmbMax)
-  int amb[kAmbMax];   // the first kAmbMax undecided token indices, ascending
+  int ngrp;           // number of groups, or -1 when they did not fit (tile recomputed exactly)
+  int pad;
+  double get[kGrp];   // per group: sum of e_t
+  double ged[kGrp];   // per group: sum of e_d
+  double pad2;
 };
 
 // ---------------------------------------------------------------------------
@@ -161,6 +166,17 @@ __device__ __forceinline__ double exp2_f64(double a) {
 // fp32 2^x on the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float exp2_f32(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Mass 2^{(l - m) c} of one token in double precision. Terms below 2^-48 of the
+// row maximum take the fp32 unit: their relative error (argument rounding
+// |a| 2^-24 plus the unit's ulp) leaves an absolute error below 2^-62 per token,
+// below the rounding of the double-precision sums they enter.
+__device__ __forceinline__ double emass(float l, float m, double c) {
+  const double a = ((double)l - (double)m) * c;
+  double e = (double)exp2_f32((float)a);
+  if (a >= -48.0) e = exp2_f64(a);
+  return e;
+}
+
 // ---------------------------------------------------------------------------
 // Wave64 / workgroup reductions.
 
@@ -184,7 +200,7 @@ hipError_t launch_accept_tree(int dt, const void* tgt, const void* dft, int V, c
                               const float* temperature, const Partial* part, int nchunk, int32_t* out,
                               int32_t* out_nodes, int32_t* num_acc, SampleJob* jobs, hipStream_t st);
 hipError_t launch_sample(int dt, const void* tgt, const void* dft, int V, int B, const SampleJob* jobs,
-                         TileRec* recs, int32_t* out, int out_width, hipStream_t st);
+                         TileRec* recs, int32_t* out, int out_width, int force_exact, hipStream_t st);
 hipError_t launch_stats_finalize(const Partial* part, int nchunk, int rows, const float* temperature,
                                  float* out_max, float* out_logz, int32_t* out_argmax, hipStream_t st);
 

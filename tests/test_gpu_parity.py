@@ -67,7 +67,8 @@ def test_chain_multi_chunk_ragged_tail(sv, dtype, V, seed):
 
 
 def test_chain_edge_shapes(sv):
-    for (B, g, V) in [(1, 0, 1), (3, 0, 50), (5, 1, 1), (4, 3, 7), (2, 2, 9), (7, 1, 8193), (1, 8, 300)]:
+    for (B, g, V) in [(1, 0, 1), (3, 0, 50), (5, 1, 1), (4, 3, 7), (2, 2, 9), (7, 1, 8193), (1, 8, 300),
+                      (6, 130, 40)]:
         for dtype in ("f32", "bf16"):
             d = inputgen.chain_inputs(B, g, V, seed=B * 1000 + g * 10 + V, dtype=dtype, scale=1.5, noise_sd=0.6,
                                       temperature=0.9)
@@ -81,6 +82,23 @@ def test_temperature_extremes(sv):
     # logits so large that |max * log2(e)/T| leaves the fp32 range
     d = inputgen.chain_inputs(8, 2, 500, seed=8, dtype="f32", scale=1e37, noise_sd=0.0, temperature=0.05)
     check_chain(sv, d, "overflowing offsets")
+
+
+def test_residual_undecided_band(sv, monkeypatch):
+    """Draft almost equal to the target with forced rejections: many tokens lie in the band where the
+    fp32 estimate of Z_t/Z_d cannot decide the residual's sign, so tiles are recomputed token by token;
+    the switch SPECVERIFY_FORCE_EXACT_RESIDUAL=1 recomputes every tile."""
+    for dtype in ("f32", "bf16"):
+        d = inputgen.chain_inputs(64, 3, 30000, seed=71, dtype=dtype, scale=2.0, noise_sd=1e-3 if dtype == "f32"
+                                  else 0.05)
+        d["u_accept"][:, 1] = 0.9999
+        out, na, ref, _ = check_chain(sv, d, f"near-identical draft {dtype}")
+        assert (na == 1).sum() > 10
+        monkeypatch.setenv("SPECVERIFY_FORCE_EXACT_RESIDUAL", "1")
+        check_chain(sv, d, f"near-identical draft {dtype}, every tile exact")
+        monkeypatch.delenv("SPECVERIFY_FORCE_EXACT_RESIDUAL")
+    monkeypatch.setenv("SPECVERIFY_FORCE_EXACT_RESIDUAL", "1")
+    check_chain(sv, inputgen.make("mid"), "mid, every tile exact")
 
 
 def test_request_errors(sv):
