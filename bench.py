@@ -14,6 +14,7 @@ recorded on the launch stream), and the CPU oracle timed on the host cores.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large]
   python bench.py --copy-calibration          # plain copy kernel of known size (PMC scale)
   python bench.py --summarize-rocprof DIR     # text summary of rocprofv3 output in DIR
+  python bench.py --write-pmc F W CF CW       # PMC traffic file from four rocprofv3 --pmc runs
 """
 from __future__ import annotations
 
@@ -176,14 +177,23 @@ def run_bench(args):
     k1_avg_ms = float(np.mean(k1_ms)) if k1_ms else float("nan")
     k1_gbps = k1_bytes / (k1_avg_ms * 1e-3) / 1e9
 
-    # CPU oracle on the host cores: the same batch (bounded: one verify step of the workload)
+    # CPU oracle on the host cores: whole verify steps of the same batch, repeated until about
+    # args.cpu_seconds of wall time have passed (at least one step)
     cores = host_cores()
-    tc = time.perf_counter()
-    ref = oracle_call(name, d, cores)
-    cpu_s = time.perf_counter() - tc
+    ref = None
+    cpu_steps = 0
+    cpu_s = 0.0
+    if not args.skip_cpu_baseline:
+        tc = time.perf_counter()
+        while cpu_steps == 0 or cpu_s < args.cpu_seconds:
+            ref = oracle_call(name, d, cores)
+            cpu_steps += 1
+            cpu_s = time.perf_counter() - tc
+        print(f"bench: oracle {cpu_steps} steps in {cpu_s:.2f} s on {cores} threads", file=sys.stderr, flush=True)
     na = outs[-1].cpu().numpy()
     out_tok = outs[0].cpu().numpy()
-    parity_ok = bool(np.array_equal(na, ref["num_accepted"]) and np.array_equal(out_tok, ref["out_tokens"]))
+    parity_ok = None if ref is None else bool(np.array_equal(na, ref["num_accepted"]) and
+                                              np.array_equal(out_tok, ref["out_tokens"]))
 
     line = {
         "metric": METRIC,
@@ -217,34 +227,90 @@ def run_bench(args):
             "avg_launch_ms": round(k1_avg_ms, 5),
             "launches_timed": len(k1_ms),
         },
-        "cpu_baseline": {
-            "value": round(positions / cpu_s, 1),
+        "cpu_baseline": None if ref is None else {
+            "value": round(positions * cpu_steps / cpu_s, 1),
             "unit": "verified draft positions/s",
             "cores": cores,
             "kind": "oracle",
-            "sample": f"one full verify step of the same workload ({positions} positions), fp64 oracle, "
-                      f"{cores} threads, {cpu_s:.2f} s wall",
+            "sample": f"{cpu_steps} full verify steps of the same batch ({positions} positions each), "
+                      f"fp64 oracle, {cores} threads, {cpu_s:.2f} s wall",
         },
         "mean_num_accepted": round(float(np.mean(na[na >= 0])), 4),
         "parity_vs_oracle": parity_ok,
     }
     print(json.dumps(line), flush=True)
-    return 0 if parity_ok else 1
+    return 0 if parity_ok is not False else 1
+
+
+COPY_BYTES = 1 << 30
 
 
 def copy_calibration(args):
-    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    """A plain copy kernel of known size (an elementwise float32 multiply by one, 1 GiB read and
+    1 GiB written per launch), for scaling the FETCH_SIZE / WRITE_SIZE counters."""
     import torch
-    n = 1 << 30
-    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    n = COPY_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    src.fill_(1)
     torch.cuda.synchronize()
     for _ in range(args.steps):
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n,
+    print(json.dumps({"copy_bytes_read_per_launch": COPY_BYTES, "copy_bytes_written_per_launch": COPY_BYTES,
                       "launches": args.steps}), flush=True)
+    return 0
+
+
+def _counter_avgs(path):
+    """{(kernel short name, counter): average value per dispatch} over rocprofv3 counter CSVs under path."""
+    agg = {}
+    for p in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
+        with open(p) as f:
+            for r in csv.DictReader(f):
+                key = (r.get("Kernel_Name", "").split("(")[0], r.get("Counter_Name"))
+                agg.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def _pick(avgs, counter, want=None):
+    """Average of `counter` for the kernel whose name contains `want` (else the largest one)."""
+    rows = [(k, v) for (k, c), v in avgs.items() if c == counter and (want is None or want in k)]
+    if not rows:
+        raise SystemExit(f"no {counter} rows" + (f" for {want}" if want else ""))
+    return max(rows, key=lambda kv: kv[1])
+
+
+def write_pmc(dirs, workload):
+    """profiles/row_stats_<workload>_pmc.json from four rocprofv3 --pmc runs: FETCH_SIZE and
+    WRITE_SIZE of the bench, then of --copy-calibration. Counter units are KiB per dispatch; each is
+    scaled by bytes/KiB of the copy kernel of known size."""
+    import inputgen
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = dirs
+    kf_name, kf = _pick(_counter_avgs(fetch_dir), "FETCH_SIZE", KERNEL)
+    kw_name, kw = _pick(_counter_avgs(write_dir), "WRITE_SIZE", KERNEL)
+    cf_name, cf = _pick(_counter_avgs(cfetch_dir), "FETCH_SIZE")
+    cw_name, cw = _pick(_counter_avgs(cwrite_dir), "WRITE_SIZE")
+    f_scale = COPY_BYTES / cf
+    w_scale = COPY_BYTES / cw
+    fetch_b = kf * f_scale
+    write_b = kw * w_scale
+    _, _, algo = workload_accounting(workload, inputgen.make(workload))
+    out = {
+        "kernel": kf_name, "workload": WORKLOAD_TEXT[workload],
+        "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
+        "copy_kernel": cf_name, "copy_fetch_kib_per_dispatch": cf, "copy_write_kib_per_dispatch": cw,
+        "copy_bytes_per_dispatch": COPY_BYTES, "fetch_scale_bytes_per_unit": f_scale,
+        "write_scale_bytes_per_unit": w_scale,
+        "hbm_fetch_bytes_per_launch": fetch_b, "hbm_write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": fetch_b + write_b, "algorithmic_bytes_per_launch": algo,
+        "traffic_over_algorithmic": (fetch_b + write_b) / algo,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    os.makedirs(os.path.dirname(PMC_FILE), exist_ok=True)
+    with open(PMC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
     return 0
 
 
@@ -285,11 +351,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="large", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall time spent timing the CPU oracle")
+    ap.add_argument("--skip-cpu-baseline", action="store_true", help="no oracle run (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-rocprof", metavar="DIR")
+    ap.add_argument("--write-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write the committed PMC traffic file from four rocprofv3 --pmc output folders")
     args = ap.parse_args()
     if args.summarize_rocprof:
         return summarize_rocprof(args.summarize_rocprof)
+    if args.write_pmc:
+        return write_pmc(args.write_pmc, args.workload)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: only one GPU is measured here; the verify step shards over requests with no "
               "communication, so N GPUs each run this same single-GPU step. Run with --gpus 1.", file=sys.stderr)

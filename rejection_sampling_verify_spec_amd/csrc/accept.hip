@@ -1,53 +1,18 @@
-// accept.hip -- acceptance scan per request.
+// accept.hip -- acceptance kernels: chains (one wave per request, the scan of
+// accept.h) and token trees (one workgroup per request).
 //
-// Chain [Primer 考点2 / 第二章]: for drafted position i the token x_i is
-// accepted when u_accept[i] * p_d,i(x_i) < p_t,i(x_i), i.e. with probability
-// min(1, p_t/p_d); the first rejected position n ends the scan. Greedy
-// requests (T == 0) accept while x_i equals the target argmax and emit the
-// argmax at n. Token trees [Primer 考点3; Edge pipeline figure]: each node is
-// tested against its parent's target row; the kept nodes are those accepted
-// together with all their ancestors; the end node is the deepest kept node.
-// p(x) = 2^{(l_x - m) c} / Z with the row statistics merged here in fp64.
-#include "sv_internal.h"
+// Token trees [Primer 考点3; Edge pipeline figure]: each node is tested against
+// its parent's target row with the chain rule (accept.h); the kept nodes are
+// those accepted together with all their ancestors; the end node is the
+// deepest kept node (lowest index among equals). Its path is emitted, and the
+// final token is drawn from the residual against the draft row of its first
+// child, or from its own target row when it has no children (bonus).
+#include "accept.h"
 
 namespace sv {
 
-struct RowStat {
-  float m;   // row max
-  double Z;  // sum 2^{(x-m)c32}
-  int idx;   // greedy argmax
-  bool ok;
-};
-
-__device__ __forceinline__ RowStat merge_row(const Partial* __restrict__ p, int nchunk, float c32, bool greedy) {
-  float M = -INFINITY;
-  int idx = -1;
-  bool nan = false;
-  for (int k = 0; k < nchunk; ++k) {
-    Partial q = p[k];
-    nan |= q.s != q.s;
-    if (q.m > M) { M = q.m; idx = q.idx; }
-  }
-  RowStat r{M, 0.0, idx, !nan && M > -INFINITY && M < INFINITY};
-  if (greedy || !r.ok) return r;
-  double c = (double)c32, Z = 0.0;
-  for (int k = 0; k < nchunk; ++k) {
-    Partial q = p[k];
-    if (q.m > -INFINITY) Z += (double)q.s * exp2_f64(((double)q.m - (double)M) * c);
-  }
-  r.Z = Z;
-  r.ok = Z > 0.0 && Z < 1e308;
-  return r;
-}
-
-// probability of token x in a row with statistics st
-template <int DT>
-__device__ __forceinline__ double prob_at(const void* base, long long row, int V, int x, const RowStat& st, float c32) {
-  float l = Elem<DT>::at(base, row * (long long)V + x);
-  return exp2_f64(((double)l - (double)st.m) * (double)c32) / st.Z;
-}
-
-constexpr int kMaxPos = 1025;  // SV_MAX_GAMMA + 1
+// ---------------------------------------------------------------------------
+// Chains (dense and ragged): one wave per request.
 
 template <int DT>
 __global__ __launch_bounds__(64) void k_accept_chain(const void* __restrict__ tgt, const void* __restrict__ dft, int V,
@@ -58,147 +23,10 @@ __global__ __launch_bounds__(64) void k_accept_chain(const void* __restrict__ tg
                                                      int32_t* __restrict__ out, int out_width,
                                                      int32_t* __restrict__ num_acc, float* __restrict__ diag,
                                                      SampleJob* __restrict__ jobs) {
-  const int b = blockIdx.x, lane = threadIdx.x;
-  __shared__ float s_pt[kMaxPos], s_pd[kMaxPos];
-  __shared__ int s_amax[kMaxPos];
-
-  // --- locate the request's rows
-  bool layout_ok = true;
-  int g;
-  long long t0, d0;
-  if (L.mode == LAYOUT_RAGGED) {
-    const int32_t* cu = L.cu;
-    bool ok = true;
-    if (lane == 0) ok = cu[0] == 0 && cu[L.B] == L.total_draft;
-    for (int k = lane; k < L.B; k += 64) {
-      int lo = cu[k], hi = cu[k + 1];
-      ok = ok && hi >= lo && hi - lo <= L.gamma;
-    }
-    layout_ok = __all(ok);
-    g = layout_ok ? cu[b + 1] - cu[b] : 0;
-    d0 = layout_ok ? cu[b] : 0;
-    t0 = d0 + b;
-  } else {
-    g = L.gamma;
-    d0 = (long long)b * g;
-    t0 = (long long)b * (g + 1);
-  }
-  int32_t* orow = out + (long long)b * out_width;
-  const float T = temperature[b];
-  bool bad = !layout_ok || !temperature_ok(T);
-  const bool greedy = T == 0.0f;
-  const float c32 = bad || greedy ? 0.0f : c32_of(T);
-
-  // --- pass A: validation and acceptance decisions. The lane holding the final
-  // position n (first rejection, or gamma) writes the sampling job from its statistics.
-  int n = g;  // first rejected position
-  bool found = false;
-  for (int base = 0; base <= g && !bad; base += 64) {
-    const int i = base + lane;
-    bool lbad = false, reject = false;
-    RowStat st{0.f, 0.0, -1, true}, sd{0.f, 0.0, -1, true};
-    if (i <= g) {
-      int x = 0;
-      float u = 0.f, usv = 0.f;
-      if (i < g) {
-        x = tokens[d0 + i];
-        if (!greedy) u = ua[d0 + i];
-      }
-      if (!greedy) usv = us[t0 + i];
-      st = merge_row(part + (t0 + i) * nchunk, nchunk, c32, greedy);
-      lbad |= !st.ok;
-      if (!greedy) lbad |= !uniform_ok(usv);
-      if (i < g) {
-        lbad |= x < 0 || x >= V;
-        if (greedy) {
-          reject = x != st.idx;
-        } else {
-          sd = merge_row(part + (L.RT + d0 + i) * nchunk, nchunk, c32, false);
-          lbad |= !sd.ok || !uniform_ok(u);
-          if (!lbad) {
-            double pt = prob_at<DT>(tgt, t0 + i, V, x, st, c32);
-            double pd = prob_at<DT>(dft, d0 + i, V, x, sd, c32);
-            reject = !((double)u * pd < pt);
-            s_pt[i] = (float)pt;
-            s_pd[i] = (float)pd;
-          }
-        }
-      }
-      if (greedy) s_amax[i] = st.idx;
-    }
-    bad = __any(lbad) || bad;
-    const unsigned long long rm = __ballot(reject && i < g);
-    if (!found && rm) {
-      n = base + __builtin_ctzll(rm);
-      found = true;
-    }
-    // job of a sampling request, written by the lane of position n
-    if (!greedy && i == n && (found || i == g)) {
-      SampleJob J;
-      J.kind = n < g ? JOB_RESIDUAL : JOB_BONUS;
-      J.pos = n;
-      J.trow = t0 + n;
-      J.drow = d0 + n;
-      J.c64 = c64_of(T);
-      J.u = us[t0 + n];
-      J.mt = st.m;
-      J.md = n < g ? sd.m : 0.0f;
-      J.rho = n < g ? st.Z / sd.Z : 0.0;
-      J.pad = 0;
-      jobs[b] = J;
-    }
-    if (found) break;
-  }
-  // validation covers every position, also those after the first rejection
-  for (int base = (n / 64 + 1) * 64; base <= g && !bad; base += 64) {
-    const int i = base + lane;
-    bool lbad = false;
-    if (i <= g) {
-      RowStat st = merge_row(part + (t0 + i) * nchunk, nchunk, c32, greedy);
-      lbad |= !st.ok;
-      if (!greedy) lbad |= !uniform_ok(us[t0 + i]);
-      if (i < g) {
-        const int x = tokens[d0 + i];
-        lbad |= x < 0 || x >= V;
-        if (!greedy) {
-          RowStat sd = merge_row(part + (L.RT + d0 + i) * nchunk, nchunk, c32, false);
-          lbad |= !sd.ok || !uniform_ok(ua[d0 + i]);
-          if (!lbad) {  // per-position probabilities for the diagnostics output
-            s_pt[i] = (float)prob_at<DT>(tgt, t0 + i, V, x, st, c32);
-            s_pd[i] = (float)prob_at<DT>(dft, d0 + i, V, x, sd, c32);
-          }
-        }
-      }
-    }
-    bad = __any(lbad) || bad;
-  }
-  __syncthreads();
-
-  // --- outputs
-  if (bad) {
-    for (int k = lane; k < out_width; k += 64) orow[k] = -1;
-    if (lane == 0) {
-      num_acc[b] = -1;
-      jobs[b].kind = JOB_NONE;
-    }
-    return;
-  }
-  for (int k = lane; k < out_width; k += 64) {
-    int v = -1;
-    if (k < n) v = tokens[d0 + k];
-    else if (k == n && greedy) v = s_amax[n];
-    orow[k] = v;
-  }
-  if (diag)
-    for (int i = lane; i < g; i += 64) {
-      const float qnan = __uint_as_float(0x7fc00000u);
-      diag[2 * (d0 + i)] = greedy ? qnan : s_pt[i];
-      diag[2 * (d0 + i) + 1] = greedy ? qnan : s_pd[i];
-    }
-  if (lane == 0) {
-    num_acc[b] = n;
-    if (greedy) jobs[b].kind = JOB_NONE;
-  }
+  __shared__ AcceptShared acc;
+  __shared__ SampleJob sj;
+  accept_chain_wave<DT>(tgt, dft, V, L, blockIdx.x, tokens, ua, us, temperature, part, nchunk, out, out_width,
+                        num_acc, diag, jobs, true, acc, sj, threadIdx.x);
 }
 
 hipError_t launch_accept_chain(int dt, const void* tgt, const void* dft, int V, const Layout& L,
@@ -336,7 +164,7 @@ __global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
     num_acc[b] = de;
     SampleJob J;
     J.pos = de;
-    J.pad = 0;
+    J.c32 = c32;
     J.trow = t0 + e;
     J.drow = 0;
     J.rho = 0.0;

@@ -163,7 +163,8 @@ int spec_verify(const void* target_logits, const void* draft_logits, int32_t dty
                           part, nchunk_for(V, dtype), out_tokens, gamma + 1, num_accepted, diag_probs, jobs,
                           st) != hipSuccess)
     return SV_EHIP;
-  if (launch_sample(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, gamma + 1, force_exact_residual(), st) != hipSuccess)
+  if (launch_sample_jobs(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, gamma + 1,
+                         force_exact_residual(), st) != hipSuccess)
     return SV_EHIP;
   return SV_OK;
 }
@@ -195,8 +196,8 @@ int spec_verify_ragged(const void* target_logits, const void* draft_logits, int3
                           part, nchunk_for(V, dtype), out_tokens, gamma_max + 1, num_accepted, diag_probs, jobs,
                           st) != hipSuccess)
     return SV_EHIP;
-  if (launch_sample(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, gamma_max + 1, force_exact_residual(), st) !=
-      hipSuccess)
+  if (launch_sample_jobs(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, gamma_max + 1,
+                         force_exact_residual(), st) != hipSuccess)
     return SV_EHIP;
   return SV_OK;
 }
@@ -227,8 +228,8 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int32_
                          u_sample, temperature, part, nchunk_for(V, dtype), out_tokens, out_nodes, num_accepted,
                          jobs, st) != hipSuccess)
     return SV_EHIP;
-  if (launch_sample(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, max_depth + 1, force_exact_residual(), st) !=
-      hipSuccess)
+  if (launch_sample_jobs(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, max_depth + 1,
+                         force_exact_residual(), st) != hipSuccess)
     return SV_EHIP;
   return SV_OK;
 }

@@ -8,14 +8,14 @@
 // except when u S lies within ~1e-13 S of a CDF boundary. The residual in
 // these units is q_j = max(0, e_t(j) - rho e_d(j)) with rho = Z_t / Z_d.
 //
-// Two kernels (a kernel boundary is the cheapest cross-workgroup hand-off on
-// this multi-die part; device-scope fences cost an L2 write-back each):
-//   k_sample_tiles (one wave per tile of kSTile tokens): Z_t and Z_d of the
-//   tile and -- with the estimate rho~ of the fp32 row statistics -- the sums
-//   over tokens with e_t > rho~(1+band) e_d of (e_t - rho~ e_d) and of e_d;
-//   tokens inside the band (the only ones whose residual sign the estimate
-//   cannot decide) are summed in groups of equal logit difference l_t - l_d,
-//   which share one likelihood ratio.
+// Two kernels, after an accept kernel has written one job per request:
+//   k_sample_tiles (one workgroup per slice of a request's tiles; each wave
+//   owns one tile of kSTile tokens at a time): per tile Z_t and Z_d and, with the estimate
+//   rho~ of the fp32 row statistics, the sums over tokens with
+//   e_t > rho~(1+band) e_d of (e_t - rho~ e_d) and of e_d; tokens inside the
+//   band (the only ones whose residual sign the estimate cannot decide) are
+//   summed in groups of equal logit difference l_t - l_d, which share one
+//   likelihood ratio.
 //   k_sample_pick (one workgroup per job): exact rho = Z_t / Z_d, exact tile
 //   masses dpos + (rho~ - rho) bpos + sum over groups of
 //   max(0, sum e_t - rho sum e_d) (tiles whose groups did not fit, or every
@@ -26,114 +26,117 @@
 
 namespace sv {
 
-constexpr int kSE = kSTile / kTPB;    // tokens per thread when a workgroup scans one tile
-constexpr int kWE = kSTile / 64;      // tokens per lane when a wave owns a tile
-constexpr int kTilesPerWG = kTPB / 64;
+constexpr int kEPL = kSTile / 64;     // tokens per lane when a wave owns a tile
+constexpr int kEPT = kSTile / kTPB;   // tokens per thread when a workgroup owns a tile
+constexpr int kWaves = kTPB / 64;
 constexpr int kList = 64;             // undecided tokens collected per tile
 
-// Fixed-order workgroup sum of doubles (same result in every thread).
-__device__ __forceinline__ double block_sum(double v, double* red) {
-  v = wave_reduce(v, [](double a, double b) { return a + b; });
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  double t = red[0];
-  for (int w = 1; w < kTPB / 64; ++w) t += red[w];
-  __syncthreads();
-  return t;
+static_assert(kEPT == 8, "a workgroup tile gives each thread 8 contiguous tokens");
+
+// Raw bits of one logit and of -inf, per storage type.
+template <int DT> __device__ __forceinline__ uint32_t raw_at(const void* rowp, int j);
+template <> __device__ __forceinline__ uint32_t raw_at<0>(const void* rowp, int j) {
+  return reinterpret_cast<const uint32_t*>(rowp)[j];
+}
+template <> __device__ __forceinline__ uint32_t raw_at<1>(const void* rowp, int j) {
+  return reinterpret_cast<const uint16_t*>(rowp)[j];
+}
+template <int DT> struct NegInf;
+template <> struct NegInf<0> { static constexpr uint32_t bits = 0xff800000u; };
+template <> struct NegInf<1> { static constexpr uint32_t bits = 0xff80u; };
+
+// n consecutive tokens starting at j as packed 16-byte vectors (element order of
+// unpack<DT>); tokens at or beyond V read as -inf. Vector loads when the whole
+// span is in range and 16-byte aligned, token by token otherwise.
+template <int DT, int NV>
+__device__ __forceinline__ void load_span(const void* rowp, int j, int V, uint4* w) {
+  constexpr int epv = Elem<DT>::kPerVec;
+  constexpr int es = sizeof(typename Elem<DT>::T);
+  const char* p = reinterpret_cast<const char*>(rowp) + (size_t)j * es;
+  if (j + NV * epv <= V && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) w[u] = reinterpret_cast<const uint4*>(p)[u];
+  } else {
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      uint32_t b[epv];
+#pragma unroll
+      for (int e = 0; e < epv; ++e) {
+        const int jj = j + u * epv + e;
+        b[e] = jj < V ? raw_at<DT>(rowp, jj) : NegInf<DT>::bits;
+      }
+      if constexpr (DT == 1) {
+        w[u] = make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+      } else {
+        w[u] = make_uint4(b[0], b[1], b[2], b[3]);
+      }
+    }
+  }
 }
 
-// A workgroup's view of one tile: tokens j = j0 + u*kTPB + tid (u < kSE); out of range -> -inf.
+// A wave's tile: lane l holds vectors u*64 + l (u < NV) of the tile, i.e. tokens
+// j0 + (u*64 + l)*epv + e.
 template <int DT>
-__device__ __forceinline__ void load_tile(const void* base, long long row, int V, int j0, float* x) {
-  const int tid = threadIdx.x;
-  const long long off = row * (long long)V;
+__device__ __forceinline__ void load_tile_wave(const void* rowp, int j0, int V, int lane,
+                                               uint4 (&w)[kEPL / Elem<DT>::kPerVec]) {
+  constexpr int epv = Elem<DT>::kPerVec;
+  constexpr int nv = kEPL / epv;
+  constexpr int es = sizeof(typename Elem<DT>::T);
+  const char* p = reinterpret_cast<const char*>(rowp) + (size_t)j0 * es;
+  if (j0 + kSTile <= V && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
 #pragma unroll
-  for (int u = 0; u < kSE; ++u) {
-    int j = j0 + u * kTPB + tid;
-    x[u] = j < V ? Elem<DT>::at(base, off + j) : -INFINITY;
+    for (int u = 0; u < nv; ++u) w[u] = reinterpret_cast<const uint4*>(p)[u * 64 + lane];
+  } else {
+#pragma unroll
+    for (int u = 0; u < nv; ++u) load_span<DT, 1>(rowp, j0 + (u * 64 + lane) * epv, V, &w[u]);
   }
 }
 
 // Per-wave list of undecided tokens of the tile pass (in a fixed order).
 struct TileLists {
-  double dl[kTilesPerWG][kList], et[kTilesPerWG][kList], ed[kTilesPerWG][kList];
+  double dl[kWaves][kList], et[kWaves][kList], ed[kWaves][kList];
 };
 
-// A wave's view of one tile: lane l holds tokens j0 + (u*64 + l)*epv + e (u < kWE/epv, e < epv),
-// read with 16-byte loads when the row is 16-byte aligned, token by token otherwise.
-template <int DT>
-__device__ __forceinline__ void load_tile_wave(const void* rowp, bool vec_ok, int j0, int V, int lane, float* x) {
-  using E = Elem<DT>;
-  constexpr int epv = E::kPerVec;
-  constexpr int nv = kWE / epv;
-  if (vec_ok) {
-    const uint4* vp = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(rowp) +
-                                                     (size_t)j0 * sizeof(typename E::T));
-#pragma unroll
-    for (int u = 0; u < nv; ++u) {
-      const int v = u * 64 + lane;
-      const int jv = j0 + v * epv;
-      if (jv + epv <= V) {
-        unpack<DT>(vp[v], x + u * epv);
-      } else {
-#pragma unroll
-        for (int e = 0; e < epv; ++e) x[u * epv + e] = jv + e < V ? E::at(rowp, jv + e) : -INFINITY;
-      }
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < nv; ++u)
-#pragma unroll
-      for (int e = 0; e < epv; ++e) {
-        const int j = j0 + (u * 64 + lane) * epv + e;
-        x[u * epv + e] = j < V ? E::at(rowp, j) : -INFINITY;
-      }
-  }
-}
-
-// One wave owns tile k; writes the tile record. Undecided tokens are appended in a fixed
-// order (element slot, then lane) through wave ballots.
-template <int DT>
-__device__ void tile_pass(const void* tgt, const void* dft, int V, const SampleJob& J, int k, TileRec* rec,
-                          TileLists& L, int wv, int lane) {
-  using E = Elem<DT>;
-  const bool res = J.kind == JOB_RESIDUAL;
-  const int j0 = k * kSTile;
+// One wave's pass over one tile; writes the tile record. Undecided tokens are
+// appended in a fixed order (element slot, then lane) through wave ballots.
+template <int DT, bool RES>
+__device__ __forceinline__ void tile_pass(const uint4* wt, const uint4* wd, const SampleJob& J, TileRec* rec,
+                                          TileLists& L, int wv, int lane) {
+  constexpr int epv = Elem<DT>::kPerVec;
+  constexpr int nv = kEPL / epv;
   const double hi = J.rho * (1.0 + kRhoBand), lo = J.rho * (1.0 - kRhoBand);
-  const void* trow = reinterpret_cast<const char*>(tgt) + (size_t)J.trow * (size_t)V * sizeof(typename E::T);
-  const void* drow = reinterpret_cast<const char*>(dft) + (size_t)J.drow * (size_t)V * sizeof(typename E::T);
-  const bool t_al = (reinterpret_cast<uintptr_t>(trow) & 15u) == 0;
-  const bool d_al = (reinterpret_cast<uintptr_t>(drow) & 15u) == 0;
   const unsigned long long below = (1ull << lane) - 1ull;
-  float xt[kWE], xd[kWE];
-  load_tile_wave<DT>(trow, t_al, j0, V, lane, xt);
-  if (res) load_tile_wave<DT>(drow, d_al, j0, V, lane, xd);
   double zt = 0.0, zd = 0.0, dp = 0.0, bp = 0.0;
   int n = 0;  // undecided tokens seen (wave-uniform)
 #pragma unroll
-  for (int i = 0; i < kWE; ++i) {
-    const double et = emass(xt[i], J.mt, J.c64);
-    zt += et;
-    if (res) {
-      const double ed = emass(xd[i], J.md, J.c64);
-      zd += ed;
-      bool und = false;
-      if (et > hi * ed) {
-        dp += et - J.rho * ed;
-        bp += ed;
-      } else {
-        und = et > 0.0 && et >= lo * ed;
-      }
-      const unsigned long long m = __ballot(und);
-      if (m) {
-        const int slot = n + __builtin_popcountll(m & below);
-        if (und && slot < kList) {
-          L.dl[wv][slot] = (double)xt[i] - (double)xd[i];
-          L.et[wv][slot] = et;
-          L.ed[wv][slot] = ed;
+  for (int u = 0; u < nv; ++u) {
+    float xt[epv], xd[epv];
+    unpack<DT>(wt[u], xt);
+    if (RES) unpack<DT>(wd[u], xd);
+#pragma unroll
+    for (int e = 0; e < epv; ++e) {
+      const double et = emass(xt[e], J.mt, J.c64, J.c32);
+      zt += et;
+      if (RES) {
+        const double ed = emass(xd[e], J.md, J.c64, J.c32);
+        zd += ed;
+        bool und = false;
+        if (et > hi * ed) {
+          dp += et - J.rho * ed;
+          bp += ed;
+        } else {
+          und = et > 0.0 && et >= lo * ed;
         }
-        n += __builtin_popcountll(m);
+        const unsigned long long m = __ballot(und);
+        if (m) {
+          const int slot = n + __builtin_popcountll(m & below);
+          if (und && slot < kList) {
+            L.dl[wv][slot] = (double)xt[e] - (double)xd[e];
+            L.et[wv][slot] = et;
+            L.ed[wv][slot] = ed;
+          }
+          n += __builtin_popcountll(m);
+        }
       }
     }
   }
@@ -141,7 +144,7 @@ __device__ void tile_pass(const void* tgt, const void* dft, int V, const SampleJ
   zt = wave_reduce(zt, add);
   int ng = 0;
   double gt = 0.0, gd = 0.0;  // lane g < ng holds group g's sums
-  if (res) {
+  if (RES) {
     zd = wave_reduce(zd, add);
     dp = wave_reduce(dp, add);
     bp = wave_reduce(bp, add);
@@ -173,6 +176,8 @@ __device__ void tile_pass(const void* tgt, const void* dft, int V, const SampleJ
           if (lane == ge) { gt += te; gd += de; }
         }
       }
+      // the lists are reused by the wave's next tile
+      __builtin_amdgcn_wave_barrier();
     }
   }
   // lanes 0..kGrp-1 hold the group sums; lane 0 writes the scalar fields
@@ -191,26 +196,42 @@ __device__ void tile_pass(const void* tgt, const void* dft, int V, const SampleJ
   }
 }
 
+// Workgroup (b, g) of G per request: tiles g*kWaves + wv + i*G*kWaves of job b.
 template <int DT>
 __global__ __launch_bounds__(kTPB) void k_sample_tiles(const void* __restrict__ tgt, const void* __restrict__ dft,
-                                                       int V, int ntile, int wg_per_job,
-                                                       const SampleJob* __restrict__ jobs,
+                                                       int V, int ntile, int G, const SampleJob* __restrict__ jobs,
                                                        TileRec* __restrict__ recs) {
-  const int b = blockIdx.x / wg_per_job, g = blockIdx.x - b * wg_per_job;
-  const SampleJob J = jobs[b];
-  if (J.kind == JOB_NONE) return;
+  const int b = blockIdx.x / G, g = blockIdx.x - b * G;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   __shared__ TileLists lists;
-  const int k = g * kTilesPerWG + wv;
-  if (k < ntile) tile_pass<DT>(tgt, dft, V, J, k, recs + (long long)b * ntile + k, lists, wv, lane);
+  const SampleJob J = jobs[b];
+  if (J.kind == JOB_NONE) return;
+  constexpr int epv = Elem<DT>::kPerVec;
+  constexpr int es = sizeof(typename Elem<DT>::T);
+  const char* trow = reinterpret_cast<const char*>(tgt) + (size_t)J.trow * (size_t)V * es;
+  const char* drow = reinterpret_cast<const char*>(dft) + (size_t)J.drow * (size_t)V * es;
+  TileRec* R = recs + (long long)b * ntile;
+  for (int k = g * kWaves + wv; k < ntile; k += G * kWaves) {
+    uint4 wt[kEPL / epv];
+    load_tile_wave<DT>(trow, k * kSTile, V, lane, wt);
+    if (J.kind == JOB_RESIDUAL) {
+      uint4 wd[kEPL / epv];
+      load_tile_wave<DT>(drow, k * kSTile, V, lane, wd);
+      tile_pass<DT, true>(wt, wd, J, R + k, lists, wv, lane);
+    } else {
+      tile_pass<DT, false>(wt, wt, J, R + k, lists, wv, lane);
+    }
+  }
 }
 
+// ---------------------------------------------------------------------------
+// Pick.
+
 struct PickSpace {
-  double red[kTPB / 64];
-  double sq[kSTile];
-  double Zt, Zd, W, thr, S;
+  double red[kWaves];
+  double Zt, Zd, W, thr;
   int tile, last_mode, any_exact, res;
-  int smin[kTPB / 64], smax[kTPB / 64];
+  int smin[kWaves], smax[kWaves];
 };
 
 // Inclusive prefix sum over the 64 lanes of a wave (fixed order).
@@ -223,10 +244,35 @@ __device__ __forceinline__ double wave_incl_scan(double v, int lane) {
   return v;
 }
 
+// Fixed-order workgroup sum of doubles (same result in every thread).
+__device__ __forceinline__ double block_sum(double v, double* red) {
+  v = wave_reduce(v, [](double a, double b) { return a + b; });
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = red[0];
+  for (int w = 1; w < kWaves; ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+// A workgroup's tile: thread tid holds the 8 contiguous tokens j0 + 8 tid + i.
+template <int DT>
+__device__ __forceinline__ void load_tile_block(const void* rowp, int j0, int V, int tid, float* x) {
+  constexpr int epv = Elem<DT>::kPerVec;
+  uint4 w[kEPT / epv];
+  load_span<DT, kEPT / epv>(rowp, j0 + tid * kEPT, V, w);
+#pragma unroll
+  for (int u = 0; u < kEPT / epv; ++u) unpack<DT>(w[u], x + u * epv);
+}
+
 template <int DT>
 __device__ void pick(const void* tgt, const void* dft, int V, int ntile, const SampleJob& J, TileRec* R,
                      int32_t* dst, int force_exact, PickSpace& P) {
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  constexpr int es = sizeof(typename Elem<DT>::T);
+  const char* trow = reinterpret_cast<const char*>(tgt) + (size_t)J.trow * (size_t)V * es;
+  const char* drow = reinterpret_cast<const char*>(dft) + (size_t)J.drow * (size_t)V * es;
   auto add = [](double a, double b) { return a + b; };
   // --- exact normalisers: wave 0, lanes over tiles, fixed-order sums
   if (wv == 0) {
@@ -260,13 +306,13 @@ __device__ void pick(const void* tgt, const void* dft, int V, int ntile, const S
     const bool all = P.any_exact == 2;
     for (int k = 0; k < ntile; ++k) {
       if (!(all || R[k].ngrp < 0)) continue;
-      float xt[kSE], xd[kSE];
-      load_tile<DT>(tgt, J.trow, V, k * kSTile, xt);
-      load_tile<DT>(dft, J.drow, V, k * kSTile, xd);
+      float xt[kEPT], xd[kEPT];
+      load_tile_block<DT>(trow, k * kSTile, V, tid, xt);
+      load_tile_block<DT>(drow, k * kSTile, V, tid, xd);
       double acc = 0.0;
 #pragma unroll
-      for (int u = 0; u < kSE; ++u) {
-        const double q = emass(xt[u], J.mt, J.c64) - rho * emass(xd[u], J.md, J.c64);
+      for (int i = 0; i < kEPT; ++i) {
+        const double q = emass(xt[i], J.mt, J.c64, J.c32) - rho * emass(xd[i], J.md, J.c64, J.c32);
         acc += q > 0.0 ? q : 0.0;
       }
       acc = block_sum(acc, P.red);
@@ -337,28 +383,23 @@ __device__ void pick(const void* tgt, const void* dft, int V, int ntile, const S
   const bool last_mode = P.last_mode != 0;
   const double thr = P.thr, Wtile = P.W;
 
-  // --- masses of the chosen tile into shared memory, then a contiguous scan per thread
-  {
-    float xt[kSE], xd[kSE];
-    load_tile<DT>(tgt, J.trow, V, tile * kSTile, xt);
-    if (res) load_tile<DT>(dft, J.drow, V, tile * kSTile, xd);
-#pragma unroll
-    for (int u = 0; u < kSE; ++u) {
-      double q = emass(xt[u], J.mt, J.c64);
-      if (res) {
-        q -= rho * emass(xd[u], J.md, J.c64);
-        q = q > 0.0 ? q : 0.0;
-      }
-      P.sq[u * kTPB + tid] = q;
-    }
-  }
-  __syncthreads();
-  double q[kSE];
+  // --- masses of the chosen tile (8 contiguous tokens per thread), then a fixed-order scan
+  double q[kEPT];
   double local = 0.0;
+  {
+    float xt[kEPT], xd[kEPT];
+    load_tile_block<DT>(trow, tile * kSTile, V, tid, xt);
+    if (res) load_tile_block<DT>(drow, tile * kSTile, V, tid, xd);
 #pragma unroll
-  for (int i = 0; i < kSE; ++i) {
-    q[i] = P.sq[tid * kSE + i];
-    local += q[i];
+    for (int i = 0; i < kEPT; ++i) {
+      double v = emass(xt[i], J.mt, J.c64, J.c32);
+      if (res) {
+        v -= rho * emass(xd[i], J.md, J.c64, J.c32);
+        v = v > 0.0 ? v : 0.0;
+      }
+      q[i] = v;
+      local += v;
+    }
   }
   const double wincl = wave_incl_scan(local, lane);
   if (lane == 63) P.red[wv] = wincl;
@@ -366,10 +407,10 @@ __device__ void pick(const void* tgt, const void* dft, int V, int ntile, const S
   double run = Wtile;
   for (int w = 0; w < wv; ++w) run += P.red[w];
   run += wincl - local;
-  const int jt = tile * kSTile + tid * kSE;
+  const int jt = tile * kSTile + tid * kEPT;
   int pk = 0x7fffffff, lastpos = -1;
 #pragma unroll
-  for (int i = 0; i < kSE; ++i) {
+  for (int i = 0; i < kEPT; ++i) {
     run += q[i];
     if (q[i] > 0.0) {
       lastpos = jt + i;
@@ -382,7 +423,7 @@ __device__ void pick(const void* tgt, const void* dft, int V, int ntile, const S
   __syncthreads();
   if (tid == 0) {
     int y = 0x7fffffff, yl = -1;
-    for (int w = 0; w < kTPB / 64; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       y = min(y, P.smin[w]);
       yl = max(yl, P.smax[w]);
     }
@@ -404,25 +445,38 @@ __global__ __launch_bounds__(kTPB) void k_sample_pick(const void* __restrict__ t
            P);
 }
 
-hipError_t launch_sample(int dt, const void* tgt, const void* dft, int V, int B, const SampleJob* jobs,
-                         TileRec* recs, int32_t* out, int out_width, int force_exact, hipStream_t st) {
-  if (B == 0) return hipSuccess;
-  const int ntile = (V + kSTile - 1) / kSTile;
-  const int wg_per_job = (ntile + kTilesPerWG - 1) / kTilesPerWG;
-  const long long grid = (long long)B * wg_per_job;
+// ---------------------------------------------------------------------------
+// Launchers.
+
+int sample_tiles(int V) { return (V + kSTile - 1) / kSTile; }
+
+// Workgroups per request in the tiles kernel: enough for about four resident
+// workgroups per compute unit over the batch, at most one per kWaves tiles.
+static int tiles_groups(int B, int ntile) {
+  constexpr int kTargetWG = 4 * 256;
+  const int maxg = (ntile + kWaves - 1) / kWaves;
+  int G = (kTargetWG + B - 1) / B;
+  return G < 1 ? 1 : (G > maxg ? maxg : G);
+}
+
+template <int DT>
+static hipError_t launch_tail(const void* tgt, const void* dft, int V, int B, SampleJob* jobs, TileRec* recs,
+                              int32_t* out, int out_width, int force_exact, hipStream_t st) {
+  const int ntile = sample_tiles(V);
+  const int G = tiles_groups(B, ntile);
+  const long long grid = (long long)B * G;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (dt == 1) {
-    hipLaunchKernelGGL(k_sample_tiles<1>, dim3((unsigned)grid), dim3(kTPB), 0, st, tgt, dft, V, ntile, wg_per_job,
-                       jobs, recs);
-    hipLaunchKernelGGL(k_sample_pick<1>, dim3(B), dim3(kTPB), 0, st, tgt, dft, V, ntile, jobs, recs, out,
-                       out_width, force_exact);
-  } else {
-    hipLaunchKernelGGL(k_sample_tiles<0>, dim3((unsigned)grid), dim3(kTPB), 0, st, tgt, dft, V, ntile, wg_per_job,
-                       jobs, recs);
-    hipLaunchKernelGGL(k_sample_pick<0>, dim3(B), dim3(kTPB), 0, st, tgt, dft, V, ntile, jobs, recs, out,
-                       out_width, force_exact);
-  }
+  hipLaunchKernelGGL(k_sample_tiles<DT>, dim3((unsigned)grid), dim3(kTPB), 0, st, tgt, dft, V, ntile, G, jobs, recs);
+  hipLaunchKernelGGL(k_sample_pick<DT>, dim3(B), dim3(kTPB), 0, st, tgt, dft, V, ntile, jobs, recs, out, out_width,
+                     force_exact);
   return hipGetLastError();
+}
+
+hipError_t launch_sample_jobs(int dt, const void* tgt, const void* dft, int V, int B, SampleJob* jobs,
+                              TileRec* recs, int32_t* out, int out_width, int force_exact, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  return dt == 1 ? launch_tail<1>(tgt, dft, V, B, jobs, recs, out, out_width, force_exact, st)
+                 : launch_tail<0>(tgt, dft, V, B, jobs, recs, out, out_width, force_exact, st);
 }
 
 }  // namespace sv

@@ -1,17 +1,18 @@
 // sv_internal.h -- shared types and device helpers of libspecverify (gfx950).
 //
-// Pipeline of one verify call (all on the caller's stream):
-//   1. row_stats   : one streaming pass over every logit row that the method
-//                    reads -> per (row, chunk) max / sum of 2^{(x-max)c} (T>0)
-//                    or max / lowest argmax (T==0), fp32, 16-byte loads.
-//   2. accept      : per request: merge chunk partials (fp64), acceptance
-//                    test per position / tree node, first rejection, greedy
-//                    outputs, and one sampling job per request.
-//   3. sample_tiles: per (job, tile of kSTile tokens): fp64 masses of the bonus
-//                    row or of the residual max(0, e_t - rho e_d) against an
-//                    estimate of rho = Z_t / Z_d.
-//   4. sample_pick : per job: exact rho, tile prefix, inverse-CDF search in the
-//                    selected tile (fp64), token written to out_tokens.
+// Pipeline of one verify call (four kernels on the caller's stream; a kernel
+// boundary is the cross-workgroup hand-off):
+//   1. row_stats : one streaming pass over every logit row that the method
+//                  reads -> per (row, chunk) max / sum of 2^{(x-max)c} (T>0)
+//                  or max / lowest argmax (T==0), fp32, 16-byte loads.
+//   2. accept    : per request: merge chunk partials (fp64), acceptance test
+//                  per position / tree node, first rejection, greedy outputs,
+//                  and one sampling job per request.
+//   3. tiles     : per (request, slice of tiles), one wave per tile of kSTile
+//                  tokens: the fp64 masses of the bonus row, or of the residual
+//                  max(0, e_t - rho e_d) against an estimate of rho = Z_t / Z_d.
+//   4. pick      : per request: exact rho, tile prefix, inverse-CDF search in
+//                  the selected tile (fp64), token written to out_tokens.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -58,7 +59,7 @@ struct SampleJob {
   double rho;         // estimate of Z_t / Z_d (residual only)
   float mt, md;       // row maxima (exact)
   float u;            // sampling uniform
-  int pad;
+  float c32;          // fl32(c64): argument of the fp32 exponential for negligible masses
 };
 
 // Per (job, tile) record of the sampling pass (fp64 sums in a fixed order).
@@ -166,14 +167,16 @@ __device__ __forceinline__ double exp2_f64(double a) {
 // fp32 2^x on the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float exp2_f32(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Mass 2^{(l - m) c} of one token in double precision. Terms below 2^-48 of the
-// row maximum take the fp32 unit: their relative error (argument rounding
-// |a| 2^-24 plus the unit's ulp) leaves an absolute error below 2^-62 per token,
-// below the rounding of the double-precision sums they enter.
-__device__ __forceinline__ double emass(float l, float m, double c) {
-  const double a = ((double)l - (double)m) * c;
-  double e = (double)exp2_f32((float)a);
-  if (a >= -48.0) e = exp2_f64(a);
+// Mass 2^{(l - m) c} of one token in double precision (c64 = c, c32 = fl32(c)).
+// Terms below 2^-50 of the row maximum (fp32 argument a32 < -50) take the fp32
+// exponential unit: the argument's error (three fp32 roundings, about
+// 2e-7 |a|) and the unit's ulp leave an absolute error below 2^-60 per token,
+// under the rounding of the double-precision sums these terms enter.
+constexpr float kTinyExp = -50.0f;
+__device__ __forceinline__ double emass(float l, float m, double c64, float c32) {
+  const float a32 = (l - m) * c32;
+  double e = (double)exp2_f32(a32);
+  if (a32 >= kTinyExp) e = exp2_f64(((double)l - (double)m) * c64);
   return e;
 }
 
@@ -199,8 +202,8 @@ hipError_t launch_accept_tree(int dt, const void* tgt, const void* dft, int V, c
                               const int32_t* tokens, const int32_t* parents, const float* ua, const float* us,
                               const float* temperature, const Partial* part, int nchunk, int32_t* out,
                               int32_t* out_nodes, int32_t* num_acc, SampleJob* jobs, hipStream_t st);
-hipError_t launch_sample(int dt, const void* tgt, const void* dft, int V, int B, const SampleJob* jobs,
-                         TileRec* recs, int32_t* out, int out_width, int force_exact, hipStream_t st);
+hipError_t launch_sample_jobs(int dt, const void* tgt, const void* dft, int V, int B, SampleJob* jobs,
+                              TileRec* recs, int32_t* out, int out_width, int force_exact, hipStream_t st);
 hipError_t launch_stats_finalize(const Partial* part, int nchunk, int rows, const float* temperature,
                                  float* out_max, float* out_logz, int32_t* out_argmax, hipStream_t st);
 
