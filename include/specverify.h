@@ -69,7 +69,7 @@ typedef enum sv_status {
 typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
 /* Largest sizes accepted (host-side validation). */
-#define SV_MAX_GAMMA 1024      /* drafted positions per request          */
+#define SV_MAX_GAMMA 256       /* drafted positions per request          */
 #define SV_MAX_TREE_NODES 1024 /* nodes per token tree (root included)    */
 #define SV_MAX_VOCAB (1 << 28)
 
@@ -180,14 +180,18 @@ int spec_verify_version(void);
 
 /*
  * Optional timing of the streaming row-statistics kernel inside the calls
- * above: when enabled, each call records a pair of HIP events around that
- * kernel on `stream`. spec_verify_timing_read returns the per-call durations
- * (ms) recorded since enabling, after the caller synchronised the stream; at
- * most `max` values are written and *count receives how many are available.
- * Enabling creates the events (host-side allocation), so it is not meant for
- * callers that forbid allocation. Not thread-safe.
+ * above. While recording is on, each call records a pair of HIP events around
+ * that kernel on `stream`. spec_verify_timing_enable(1) starts or resumes
+ * recording, spec_verify_timing_enable(0) pauses it (recorded pairs are kept),
+ * spec_verify_timing_reset() forgets them. spec_verify_timing_read returns the
+ * recorded per-call durations (ms), after the caller synchronised the stream;
+ * at most `max` values are written and *count receives how many are available
+ * (at most 4096 are kept). The first enable creates the events (host-side
+ * allocation), so it is not meant for callers that forbid allocation. Not
+ * thread-safe.
  */
 int spec_verify_timing_enable(int enable);
+int spec_verify_timing_reset(void);
 int spec_verify_timing_read(float* ms_out, int32_t max, int32_t* count);
 
 #ifdef __cplusplus

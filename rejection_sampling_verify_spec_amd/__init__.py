@@ -6,7 +6,8 @@ the C ABI in ``include/specverify.h``); ``specverify`` is its ctypes binding.
 from .specverify import (  # noqa: F401
     SV_BF16, SV_F32, SpecVerifyError, Workspace, row_softmax_stats, spec_row_softmax_stats,
     spec_row_softmax_stats_workspace_bytes, spec_verify, spec_verify_ragged, spec_verify_ragged_workspace_bytes,
-    spec_verify_strerror, spec_verify_timing_enable, spec_verify_timing_read, spec_verify_tree,
+    spec_verify_strerror, spec_verify_timing_enable, spec_verify_timing_read,
+    spec_verify_timing_reset, spec_verify_tree,
     spec_verify_tree_workspace_bytes, spec_verify_version, spec_verify_workspace_bytes, verify_chain, verify_ragged,
     verify_tree,
 )

@@ -1,5 +1,5 @@
-// accept.hip -- acceptance kernels: chains (one wave per request, the scan of
-// accept.h) and token trees (one workgroup per request).
+// accept.hip -- acceptance walk of token trees (one workgroup per request);
+// chains are scanned inside the finishing kernel (finish.hip).
 //
 // Token trees [Primer 考点3; Edge pipeline figure]: each node is tested against
 // its parent's target row with the chain rule (accept.h); the kept nodes are
@@ -10,38 +10,6 @@
 #include "accept.h"
 
 namespace sv {
-
-// ---------------------------------------------------------------------------
-// Chains (dense and ragged): one wave per request.
-
-template <int DT>
-__global__ __launch_bounds__(64) void k_accept_chain(const void* __restrict__ tgt, const void* __restrict__ dft, int V,
-                                                     Layout L, const int32_t* __restrict__ tokens,
-                                                     const float* __restrict__ ua, const float* __restrict__ us,
-                                                     const float* __restrict__ temperature,
-                                                     const Partial* __restrict__ part, int nchunk,
-                                                     int32_t* __restrict__ out, int out_width,
-                                                     int32_t* __restrict__ num_acc, float* __restrict__ diag,
-                                                     SampleJob* __restrict__ jobs) {
-  __shared__ AcceptShared acc;
-  __shared__ SampleJob sj;
-  accept_chain_wave<DT>(tgt, dft, V, L, blockIdx.x, tokens, ua, us, temperature, part, nchunk, out, out_width,
-                        num_acc, diag, jobs, true, acc, sj, threadIdx.x);
-}
-
-hipError_t launch_accept_chain(int dt, const void* tgt, const void* dft, int V, const Layout& L,
-                               const int32_t* tokens, const float* ua, const float* us, const float* temperature,
-                               const Partial* part, int nchunk, int32_t* out, int out_width, int32_t* num_acc,
-                               float* diag, SampleJob* jobs, hipStream_t st) {
-  if (L.B == 0) return hipSuccess;
-  if (dt == 1)
-    hipLaunchKernelGGL(k_accept_chain<1>, dim3(L.B), dim3(64), 0, st, tgt, dft, V, L, tokens, ua, us, temperature,
-                       part, nchunk, out, out_width, num_acc, diag, jobs);
-  else
-    hipLaunchKernelGGL(k_accept_chain<0>, dim3(L.B), dim3(64), 0, st, tgt, dft, V, L, tokens, ua, us, temperature,
-                       part, nchunk, out, out_width, num_acc, diag, jobs);
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------
 // Token trees: one workgroup per request, one thread per node.
@@ -165,6 +133,9 @@ __global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
     SampleJob J;
     J.pos = de;
     J.c32 = c32;
+    J.skip = 0ull;
+    J.chunk_tiles = 0;
+    J.pad = 0;
     J.trow = t0 + e;
     J.drow = 0;
     J.rho = 0.0;

@@ -159,12 +159,9 @@ int spec_verify(const void* target_logits, const void* draft_logits, int32_t dty
   TileRec* recs = reinterpret_cast<TileRec*>(ws + cv.recs);
   Layout L{LAYOUT_DENSE, B, gamma, nullptr, 0, RT, RD};
   if ((rc = launch_stats(dtype, target_logits, draft_logits, V, L, temperature, part, st))) return rc;
-  if (launch_accept_chain(dtype, target_logits, draft_logits, V, L, draft_tokens, u_accept, u_sample, temperature,
-                          part, nchunk_for(V, dtype), out_tokens, gamma + 1, num_accepted, diag_probs, jobs,
-                          st) != hipSuccess)
-    return SV_EHIP;
-  if (launch_sample_jobs(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, gamma + 1,
-                         force_exact_residual(), st) != hipSuccess)
+  if (launch_finish_chain(dtype, target_logits, draft_logits, V, L, draft_tokens, u_accept, u_sample, temperature,
+                          part, nchunk_for(V, dtype), chunk_vecs(), out_tokens, gamma + 1, num_accepted, diag_probs, jobs,
+                          recs, force_exact_residual(), st) != hipSuccess)
     return SV_EHIP;
   return SV_OK;
 }
@@ -192,12 +189,9 @@ int spec_verify_ragged(const void* target_logits, const void* draft_logits, int3
   TileRec* recs = reinterpret_cast<TileRec*>(ws + cv.recs);
   Layout L{LAYOUT_RAGGED, B, gamma_max, cu_gamma, total_draft, RT, RD};
   if ((rc = launch_stats(dtype, target_logits, draft_logits, V, L, temperature, part, st))) return rc;
-  if (launch_accept_chain(dtype, target_logits, draft_logits, V, L, draft_tokens, u_accept, u_sample, temperature,
-                          part, nchunk_for(V, dtype), out_tokens, gamma_max + 1, num_accepted, diag_probs, jobs,
-                          st) != hipSuccess)
-    return SV_EHIP;
-  if (launch_sample_jobs(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, gamma_max + 1,
-                         force_exact_residual(), st) != hipSuccess)
+  if (launch_finish_chain(dtype, target_logits, draft_logits, V, L, draft_tokens, u_accept, u_sample, temperature,
+                          part, nchunk_for(V, dtype), chunk_vecs(), out_tokens, gamma_max + 1, num_accepted, diag_probs, jobs,
+                          recs, force_exact_residual(), st) != hipSuccess)
     return SV_EHIP;
   return SV_OK;
 }
@@ -228,7 +222,7 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int32_
                          u_sample, temperature, part, nchunk_for(V, dtype), out_tokens, out_nodes, num_accepted,
                          jobs, st) != hipSuccess)
     return SV_EHIP;
-  if (launch_sample_jobs(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, max_depth + 1,
+  if (launch_finish_jobs(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, max_depth + 1,
                          force_exact_residual(), st) != hipSuccess)
     return SV_EHIP;
   return SV_OK;
@@ -276,11 +270,16 @@ int spec_verify_timing_enable(int enable) {
       for (auto& e : g_timing.ev)
         if (hipEventCreate(&e) != hipSuccess) return SV_EHIP;
     }
-    g_timing.used = 0;
     g_timing.on = true;
   } else {
     g_timing.on = false;
   }
+  return SV_OK;
+}
+
+int spec_verify_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing.used = 0;
   return SV_OK;
 }
 

@@ -1,18 +1,16 @@
 // sv_internal.h -- shared types and device helpers of libspecverify (gfx950).
 //
-// Pipeline of one verify call (four kernels on the caller's stream; a kernel
-// boundary is the cross-workgroup hand-off):
+// Pipeline of one verify call (kernels on the caller's stream; a kernel
+// boundary is the only hand-off between workgroups):
 //   1. row_stats : one streaming pass over every logit row that the method
 //                  reads -> per (row, chunk) max / sum of 2^{(x-max)c} (T>0)
 //                  or max / lowest argmax (T==0), fp32, 16-byte loads.
-//   2. accept    : per request: merge chunk partials (fp64), acceptance test
-//                  per position / tree node, first rejection, greedy outputs,
-//                  and one sampling job per request.
-//   3. tiles     : per (request, slice of tiles), one wave per tile of kSTile
-//                  tokens: the fp64 masses of the bonus row, or of the residual
-//                  max(0, e_t - rho e_d) against an estimate of rho = Z_t / Z_d.
-//   4. pick      : per request: exact rho, tile prefix, inverse-CDF search in
-//                  the selected tile (fp64), token written to out_tokens.
+//   2. accept    : one workgroup per request: merge of the chunk partials in
+//                  fp64, acceptance test per position (or tree node), first
+//                  rejection, greedy outputs, one sampling job per request.
+//   3. tiles     : several workgroups per request: per tile of the residual or
+//                  bonus row, fp32 triage and, where masses matter, fp64 sums.
+//   4. pick      : one workgroup per request: inverse-CDF search (fp64).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -60,6 +58,9 @@ struct SampleJob {
   float mt, md;       // row maxima (exact)
   float u;            // sampling uniform
   float c32;          // fl32(c64): argument of the fp32 exponential for negligible masses
+  unsigned long long skip;  // bonus: row chunks whose tiles are not read (bit k = chunk k)
+  int chunk_tiles;    // tiles per chunk when skip != 0
+  int pad;
 };
 
 // Per (job, tile) record of the sampling pass (fp64 sums in a fixed order).
@@ -71,12 +72,18 @@ struct TileRec {
   double zd;          // sum of e_d (residual); the exact tile mass once the pick has run
   double dpos;        // sum over decided-positive tokens of (e_t - rho~ e_d)
   double bpos;        // sum over decided-positive tokens of e_d
-  int ngrp;           // number of groups, or -1 when they did not fit (tile recomputed exactly)
+  int ngrp;           // number of groups (>= 0), or one of the Rec* codes below
   int pad;
   double get[kGrp];   // per group: sum of e_t
   double ged[kGrp];   // per group: sum of e_d
   double pad2;
 };
+
+// TileRec::ngrp codes.
+constexpr int kRecOverflow = -1;    // undecided tokens did not fit: the pick recomputes the tile
+constexpr int kRecRecomputed = -2;  // recomputed by the pick: exact residual mass in zd
+constexpr int kRecChunkHead = -4;   // first tile of a skipped chunk: zt holds the whole chunk's mass
+constexpr int kRecChunkBody = -5;   // other tiles of a skipped chunk: mass 0 here
 
 // ---------------------------------------------------------------------------
 // Temperature handling shared by every kernel: identical expressions give
@@ -194,15 +201,16 @@ __device__ __forceinline__ T wave_reduce(T v, F op) {
 hipError_t launch_row_stats(int dt, const void* tgt, const void* dft, int V, const Layout& L,
                             const float* temperature, int chunk_vecs, int nchunk, Partial* part,
                             hipStream_t st);
-hipError_t launch_accept_chain(int dt, const void* tgt, const void* dft, int V, const Layout& L,
-                               const int32_t* tokens, const float* ua, const float* us, const float* temperature,
-                               const Partial* part, int nchunk, int32_t* out, int out_width, int32_t* num_acc,
-                               float* diag, SampleJob* jobs, hipStream_t st);
 hipError_t launch_accept_tree(int dt, const void* tgt, const void* dft, int V, const Layout& L, int max_depth,
                               const int32_t* tokens, const int32_t* parents, const float* ua, const float* us,
                               const float* temperature, const Partial* part, int nchunk, int32_t* out,
                               int32_t* out_nodes, int32_t* num_acc, SampleJob* jobs, hipStream_t st);
-hipError_t launch_sample_jobs(int dt, const void* tgt, const void* dft, int V, int B, SampleJob* jobs,
+hipError_t launch_finish_chain(int dt, const void* tgt, const void* dft, int V, const Layout& L,
+                               const int32_t* tokens, const float* ua, const float* us, const float* temperature,
+                               const Partial* part, int nchunk, int chunk_vecs, int32_t* out, int out_width,
+                               int32_t* num_acc, float* diag, SampleJob* jobs, TileRec* recs, int force_exact,
+                               hipStream_t st);
+hipError_t launch_finish_jobs(int dt, const void* tgt, const void* dft, int V, int B, SampleJob* jobs,
                               TileRec* recs, int32_t* out, int out_width, int force_exact, hipStream_t st);
 hipError_t launch_stats_finalize(const Partial* part, int nchunk, int rows, const float* temperature,
                                  float* out_max, float* out_logz, int32_t* out_argmax, hipStream_t st);

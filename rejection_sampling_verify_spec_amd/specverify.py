@@ -50,6 +50,8 @@ _lib.spec_verify_strerror.restype = ctypes.c_char_p
 _lib.spec_verify_version.restype = ctypes.c_int
 _lib.spec_verify_timing_enable.argtypes = [ctypes.c_int]
 _lib.spec_verify_timing_enable.restype = ctypes.c_int
+_lib.spec_verify_timing_reset.argtypes = []
+_lib.spec_verify_timing_reset.restype = ctypes.c_int
 _lib.spec_verify_timing_read.argtypes = [_P, _I32, _P]
 _lib.spec_verify_timing_read.restype = ctypes.c_int
 
@@ -142,11 +144,17 @@ def spec_row_softmax_stats(logits, dtype, rows, V, temperature, out_max, out_log
 
 
 def spec_verify_timing_enable(enable: bool) -> int:
+    """Start/resume (True) or pause (False) event timing of the row-statistics kernel."""
     return _lib.spec_verify_timing_enable(1 if enable else 0)
 
 
+def spec_verify_timing_reset() -> int:
+    """Forget the recorded durations."""
+    return _lib.spec_verify_timing_reset()
+
+
 def spec_verify_timing_read(max_n: int = 4096):
-    """Per-call durations (ms) of the row-statistics kernel since enabling."""
+    """Recorded per-call durations (ms) of the row-statistics kernel."""
     buf = (ctypes.c_float * max_n)()
     cnt = ctypes.c_int32(0)
     _check(_lib.spec_verify_timing_read(ctypes.cast(buf, _P), max_n, ctypes.addressof(cnt)))

@@ -123,6 +123,31 @@ def test_request_errors(sv):
     assert (out[na == -1] == -1).all()
 
 
+def test_bonus_negligible_chunks(sv):
+    """Near one-hot bonus rows: every chunk of the streaming pass but the last holds masses far below
+    2^-50 of the row maximum, so the draw takes those chunks' mass from the streaming pass instead of
+    reading them again. u_sample = 0 puts u*S at 0, i.e. on the first token with positive mass, which
+    lies inside such a chunk: the pick then walks the chunk token by token. Other uniforms land on the
+    maximum. Row maxima sit in the last chunk; drafts equal the target, so every draft is accepted."""
+    rng = np.random.default_rng(21)
+    B, g, V = 24, 2, 70000
+    for dtype in ("f32", "bf16"):
+        tgt = np.full((B, g + 1, V), -40.0, np.float32)
+        tgt += rng.integers(0, 4, size=tgt.shape).astype(np.float32) * 0.25
+        tgt[:, :, V - 7] = 0.0
+        tgt[:, :, V - 3] = -1.5
+        T = np.full(B, 1.0, np.float32)
+        T[1::4] = 0.9
+        arr = tgt if dtype == "f32" else (tgt.view(np.uint32) >> 16).astype(np.uint16)
+        d = dict(target=arr, draft=arr[:, :g].copy(), draft_tokens=np.full((B, g), V - 7, np.int32),
+                 u_accept=rng.random((B, g)).astype(np.float32) * 0.99,
+                 u_sample=np.zeros((B, g + 1), np.float32), temperature=T)
+        d["u_sample"][B // 2:, g] = rng.random(B - B // 2).astype(np.float32)
+        out, na, ref, _ = check_chain(sv, d, f"negligible chunks {dtype}")
+        assert (na == g).all()
+        assert (out[: B // 2, g] < V - 7).all()  # drawn inside a chunk that was not read again
+
+
 def test_greedy_ties(sv):
     """Integer logits: many tied maxima; the lowest index must win everywhere."""
     rng = np.random.default_rng(5)
