@@ -402,86 +402,43 @@ __device__ __forceinline__ void write_rec(TileRec* rec, double zt, double zd, do
   }
 }
 
-// Triage of one tile by one wave, in fp32 for every token.
-//
-// A token whose mass is below 2^-50 of its row maximum in both rows (fp32
-// argument a < kTinyExp) and, for a residual, whose likelihood ratio lies
-// outside twice the band around rho~, contributes terms whose fp32 rounding is
-// below 2^-70 of the row maximum. A tile made only of such tokens is summed
-// here with the decisions the exact pass would take, and its record is final;
-// returns false. Any other tile (some mass is significant, or some ratio is
-// near rho~) returns true and needs the exact pass.
-template <int DT, bool RES>
-__device__ __forceinline__ bool tile_triage(const uint4 (&wt)[kEPL / Elem<DT>::kPerVec],
-                                            const uint4 (&wd)[kEPL / Elem<DT>::kPerVec], const SampleJob& J,
-                                            TileRec* rec, int lane) {
-  constexpr int epv = Elem<DT>::kPerVec;
-  constexpr int nv = kEPL / epv;
-  const float mt = J.mt, md = J.md, c32 = J.c32;
-  const float rho32 = (float)J.rho;
-  const float hi32 = (float)(J.rho * (1.0 + 2.0 * kRhoBand)), lo32 = (float)(J.rho * (1.0 - 2.0 * kRhoBand));
-  float st = 0.f, sd = 0.f, sdp = 0.f, sbp = 0.f;
-  bool slow = false;
-#pragma unroll
-  for (int u = 0; u < nv; ++u) {
-    float xt[epv], xd[epv];
-    unpack<DT>(wt[u], xt);
-    if (RES) unpack<DT>(wd[u], xd);
-#pragma unroll
-    for (int e = 0; e < epv; ++e) {
-      const float at = (xt[e] - mt) * c32;
-      const float et = exp2_f32(at);
-      slow |= at >= kTinyExp;
-      st += et;
-      if (RES) {
-        const float ad = (xd[e] - md) * c32;
-        const float ed = exp2_f32(ad);
-        slow |= ad >= kTinyExp;
-        sd += ed;
-        if (et > hi32 * ed) {
-          sdp += et - rho32 * ed;
-          sbp += ed;
-        } else {
-          slow |= et > 0.f && et >= lo32 * ed;
-        }
-      }
-    }
-  }
-  if (__any(slow)) return true;
-  auto add = [](double a, double b) { return a + b; };
-  const double zt = wave_reduce((double)st, add);
-  double zd = 0.0, dp = 0.0, bp = 0.0;
-  if (RES) {
-    zd = wave_reduce((double)sd, add);
-    dp = wave_reduce((double)sdp, add);
-    bp = wave_reduce((double)sbp, add);
-  }
-  write_rec(rec, zt, zd, dp, bp, 0, 0.0, 0.0, lane);
-  return false;
-}
+// LDS copy of the waves' tiles (raw 16-byte vectors [u][lane]) for the per-token
+// double-precision fixup; residual draws also stage the draft row.
+template <int DT>
+struct TileStage {
+  static constexpr int nv = kEPL / Elem<DT>::kPerVec;
+  uint4 t[kVW][nv][64];
+  uint4 d[kVW][nv][64];
+};
 
-// Exact (fp64) treatment of one token of the exact pass.
+// Double-precision treatment of one flagged token (has == false: this lane has
+// none left this step, but still takes part in the wave ballot).
 struct ExactAcc {
   double zt, zd, dp, bp;
   int n;  // undecided tokens seen (wave-uniform)
 };
 
 template <bool RES>
-__device__ __forceinline__ void exact_token(float xt, float xd, const SampleJob& J, double hi, double lo,
+__device__ __forceinline__ void exact_token(bool has, float xt, float xd, const SampleJob& J, double hi, double lo,
                                             unsigned long long below, ExactAcc& A, TileLists& L, int wv,
                                             const double* tab) {
-  const double et = emass_t(xt, J.mt, J.c64, J.c32, tab);
-  A.zt += et;
-  if (!RES) return;
-  const double ed = emass_t(xd, J.md, J.c64, J.c32, tab);
-  A.zd += ed;
+  double et = 0.0, ed = 0.0;
   bool und = false;
-  if (et > hi * ed) {
-    A.dp += et - J.rho * ed;
-    A.bp += ed;
-  } else {
-    und = et > 0.0 && et >= lo * ed;
+  if (has) {
+    et = emass_t(xt, J.mt, J.c64, J.c32, tab);
+    A.zt += et;
+    if (RES) {
+      ed = emass_t(xd, J.md, J.c64, J.c32, tab);
+      A.zd += ed;
+      if (et > hi * ed) {
+        A.dp += et - J.rho * ed;
+        A.bp += ed;
+      } else {
+        und = et > 0.0 && et >= lo * ed;
+      }
+    }
   }
+  if (!RES) return;
   const unsigned long long m = __ballot(und);
   if (m) {
     const int slot = A.n + __builtin_popcountll(m & below);
@@ -494,55 +451,101 @@ __device__ __forceinline__ void exact_token(float xt, float xd, const SampleJob&
   }
 }
 
-// Exact pass of one tile by one wave, on the registers the triage used:
-// double-precision masses, the band decisions in double precision, and the
-// undecided tokens appended to a list in a fixed order (vector, token, lane)
-// through wave ballots. Inside a vector, one token per step (the next one is
-// shifted into the low bits), so that few double-precision temporaries are
-// live at once.
+// Token e of a staged 16-byte vector, read from LDS.
+template <int DT>
+__device__ __forceinline__ float staged_at(const uint4& v, int e) {
+  if constexpr (DT == 1) {
+    const uint16_t bits = reinterpret_cast<const uint16_t*>(&v)[e];
+    return __uint_as_float((uint32_t)bits << 16);
+  } else {
+    return reinterpret_cast<const float*>(&v)[e];
+  }
+}
+
+// Pass over one tile by one wave; writes the tile record. The lane holds the
+// tile's 16-byte vectors u*64 + lane (u < nv) in wt (and wd); its token (u, e)
+// is token j0 + (u*64 + lane)*epv + e.
+//
+// Every token first goes through fp32. A token whose mass is below 2^-50 of its
+// row maximum in both rows (fp32 argument a < kTinyExp) and, for a residual,
+// whose likelihood ratio lies outside twice the band around rho~ contributes
+// terms whose fp32 rounding is below 2^-70 of the row maximum: it is summed,
+// and for a residual decided, in fp32. Every other token is flagged. The
+// lane's flagged tokens are then taken one per step in double precision (fp64
+// masses; the band decision in fp64; undecided tokens appended to a list in a
+// fixed order (step, lane) through wave ballots), with their logits read back
+// from an LDS copy of the tile. Near one-hot rows flag a handful of tokens per
+// row; rows where every mass is significant flag every token.
 template <int DT, bool RES>
-__device__ __forceinline__ void tile_exact(const uint4 (&wt)[kEPL / Elem<DT>::kPerVec],
-                                           const uint4 (&wd)[kEPL / Elem<DT>::kPerVec], const SampleJob& J,
-                                           TileRec* rec, TileLists& L, const double* tab, int wv, int lane) {
+__device__ __forceinline__ void tile_pass(const uint4 (&wt)[kEPL / Elem<DT>::kPerVec],
+                                          const uint4 (&wd)[kEPL / Elem<DT>::kPerVec], const SampleJob& J,
+                                          TileRec* rec, TileLists& L, TileStage<DT>& G, const double* tab, int wv,
+                                          int lane) {
   constexpr int epv = Elem<DT>::kPerVec;
   constexpr int nv = kEPL / epv;
-  const double hi = J.rho * (1.0 + kRhoBand), lo = J.rho * (1.0 - kRhoBand);
-  const unsigned long long below = (1ull << lane) - 1ull;
-  ExactAcc A{0.0, 0.0, 0.0, 0.0, 0};
-  // the vectors rotate through q*[0] so that every register index is a constant
-  uint4 qt[nv], qd[nv];
+  static_assert(nv * epv <= 32, "one flag bit per token of the lane");
+  const float mt = J.mt, md = J.md, c32 = J.c32;
+  float st = 0.f, sd = 0.f, sdp = 0.f, sbp = 0.f;
+  uint32_t flags = 0u;
+  {
+    const float rho32 = (float)J.rho;
+    const float hi32 = (float)(J.rho * (1.0 + 2.0 * kRhoBand)), lo32 = (float)(J.rho * (1.0 - 2.0 * kRhoBand));
 #pragma unroll
-  for (int u = 0; u < nv; ++u) {
-    qt[u] = wt[u];
-    qd[u] = RES ? wd[u] : make_uint4(0u, 0u, 0u, 0u);
-  }
-#pragma unroll 1
-  for (int u = 0; u < nv; ++u) {
-    uint4 ct = qt[0], cd = qd[0];
+    for (int u = 0; u < nv; ++u) {
+      float xt[epv], xd[epv];
+      unpack<DT>(wt[u], xt);
+      if (RES) unpack<DT>(wd[u], xd);
 #pragma unroll
-    for (int k = 0; k + 1 < nv; ++k) {
-      qt[k] = qt[k + 1];
-      if (RES) qd[k] = qd[k + 1];
-    }
-#pragma unroll 1
-    for (int e = 0; e < epv; ++e) {
-      float xt, xd;
-      if (DT == 1) {
-        xt = __uint_as_float(ct.x << 16);
-        xd = __uint_as_float(cd.x << 16);
-        ct = make_uint4(__builtin_amdgcn_alignbit(ct.y, ct.x, 16), __builtin_amdgcn_alignbit(ct.z, ct.y, 16),
-                        __builtin_amdgcn_alignbit(ct.w, ct.z, 16), ct.w >> 16);
-        if (RES)
-          cd = make_uint4(__builtin_amdgcn_alignbit(cd.y, cd.x, 16), __builtin_amdgcn_alignbit(cd.z, cd.y, 16),
-                          __builtin_amdgcn_alignbit(cd.w, cd.z, 16), cd.w >> 16);
-      } else {
-        xt = __uint_as_float(ct.x);
-        xd = __uint_as_float(cd.x);
-        ct = make_uint4(ct.y, ct.z, ct.w, 0u);
-        if (RES) cd = make_uint4(cd.y, cd.z, cd.w, 0u);
+      for (int e = 0; e < epv; ++e) {
+        const float at = (xt[e] - mt) * c32;
+        const float et = exp2_f32(at);
+        bool flag = at >= kTinyExp;
+        if (RES) {
+          const float ad = (xd[e] - md) * c32;
+          const float ed = exp2_f32(ad);
+          flag |= ad >= kTinyExp;
+          const bool pos = et > hi32 * ed;
+          flag |= !pos && et > 0.f && et >= lo32 * ed;
+          if (!flag) {
+            st += et;
+            sd += ed;
+            if (pos) {
+              sdp += et - rho32 * ed;
+              sbp += ed;
+            }
+          }
+        } else if (!flag) {
+          st += et;
+        }
+        flags |= (uint32_t)flag << (u * epv + e);
       }
-      exact_token<RES>(xt, xd, J, hi, lo, below, A, L, wv, tab);
     }
+  }
+  ExactAcc A{(double)st, (double)sd, (double)sdp, (double)sbp, 0};
+  if (__any(flags != 0u)) {
+#pragma unroll
+    for (int u = 0; u < nv; ++u) {
+      G.t[wv][u][lane] = wt[u];
+      if (RES) G.d[wv][u][lane] = wd[u];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    const double hi = J.rho * (1.0 + kRhoBand), lo = J.rho * (1.0 - kRhoBand);
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll 1
+    while (__any(flags != 0u)) {
+      const bool has = flags != 0u;
+      const int i = has ? __builtin_ctz(flags) : 0;
+      flags &= flags - 1u;
+      float xt = 0.f, xd = 0.f;
+      if (has) {
+        xt = staged_at<DT>(G.t[wv][i / epv][lane], i % epv);
+        if (RES) xd = staged_at<DT>(G.d[wv][i / epv][lane], i % epv);
+      }
+      exact_token<RES>(has, xt, xd, J, hi, lo, below, A, L, wv, tab);
+    }
+    // the stage and the lists are reused by the wave's next tile
+    __builtin_amdgcn_wave_barrier();
   }
   auto add = [](double a, double b) { return a + b; };
   const double zt = wave_reduce(A.zt, add);
@@ -554,7 +557,7 @@ __device__ __forceinline__ void tile_exact(const uint4 (&wt)[kEPL / Elem<DT>::kP
     bp = wave_reduce(A.bp, add);
     const int n = A.n;
     if (n > kList) {
-      ng = -1;
+      ng = kRecOverflow;
     } else if (n > 0) {
       // the wave's list entries are complete before lanes read them
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -572,7 +575,7 @@ __device__ __forceinline__ void tile_exact(const uint4 (&wt)[kEPL / Elem<DT>::kP
       ng = __builtin_popcountll(leaders);
       const int grp = __builtin_popcountll(leaders & ((1ull << first) - 1ull));
       if (ng > kGrp) {
-        ng = -1;
+        ng = kRecOverflow;
       } else {
         // group sums in list order: lane g accumulates the entries of group g
         for (int e = 0; e < n; ++e) {
@@ -591,16 +594,15 @@ __device__ __forceinline__ void tile_exact(const uint4 (&wt)[kEPL / Elem<DT>::kP
 // One wave's tile k (if below ntile and not in a skipped chunk).
 template <int DT, bool RES>
 __device__ __forceinline__ void wave_tile(const char* trow, const char* drow, int V, int ntile, int k,
-                                          const SampleJob& J, TileRec* R, TileLists& L, const double* tab, int wv,
-                                          int lane) {
+                                          const SampleJob& J, TileRec* R, TileLists& L, TileStage<DT>& G,
+                                          const double* tab, int wv, int lane) {
   constexpr int nv = kEPL / Elem<DT>::kPerVec;
   if (k >= ntile) return;
   if (!RES && J.skip && ((J.skip >> (k / J.chunk_tiles)) & 1ull)) return;
   uint4 wt[nv], wd[nv];
   load_tile_wave<DT>(trow, k * kSTile, V, lane, wt);
   if (RES) load_tile_wave<DT>(drow, k * kSTile, V, lane, wd);
-  if (tile_triage<DT, RES>(wt, RES ? wd : wt, J, R + k, lane))
-    tile_exact<DT, RES>(wt, RES ? wd : wt, J, R + k, L, tab, wv, lane);
+  tile_pass<DT, RES>(wt, RES ? wd : wt, J, R + k, L, G, tab, wv, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -891,6 +893,7 @@ __global__ __launch_bounds__(kVT) void k_tiles(const void* __restrict__ tgt, con
                                                int G, const SampleJob* __restrict__ jobs,
                                                TileRec* __restrict__ recs) {
   __shared__ TileLists lists;
+  __shared__ TileStage<DT> stage;
   __shared__ double exp2tab[64];
   __shared__ SampleJob sj;
   if (threadIdx.x < 64) exp2tab[threadIdx.x] = exp2_f64((double)threadIdx.x * 0.015625);
@@ -907,9 +910,9 @@ __global__ __launch_bounds__(kVT) void k_tiles(const void* __restrict__ tgt, con
   TileRec* R = recs + (long long)b * ntile;
   for (int base = g * kTPG; base < ntile; base += G * kTPG) {
     if (J.kind == JOB_RESIDUAL)
-      wave_tile<DT, true>(trow, drow, V, ntile, base + wv, J, R, lists, exp2tab, wv, lane);
+      wave_tile<DT, true>(trow, drow, V, ntile, base + wv, J, R, lists, stage, exp2tab, wv, lane);
     else
-      wave_tile<DT, false>(trow, trow, V, ntile, base + wv, J, R, lists, exp2tab, wv, lane);
+      wave_tile<DT, false>(trow, trow, V, ntile, base + wv, J, R, lists, stage, exp2tab, wv, lane);
   }
 }
 
