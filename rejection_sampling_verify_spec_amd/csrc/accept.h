@@ -20,28 +20,29 @@ struct RowStat {
 __device__ __forceinline__ RowStat merge_row(const Partial* __restrict__ p, int nchunk, float c32, bool greedy) {
   float M = -INFINITY;
   int idx = -1;
-  bool nan = false;
+  bool bad = false;
   double Z = 0.0;
   const double c = (double)c32;
   for (int k0 = 0; k0 < nchunk; k0 += 4) {
     Partial q[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) q[u] = k0 + u < nchunk ? p[k0 + u] : Partial{-INFINITY, 0.0f, -1, 0};
+    for (int u = 0; u < 4; ++u) q[u] = k0 + u < nchunk ? read_partial(p + k0 + u) : Partial{-INFINITY, 1u};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      nan |= q[u].s != q[u].s;
+      bad |= partial_bad(q[u], greedy);
+      const float s = partial_s(q[u]);
       if (q[u].m > M) {
         // new running maximum: rescale what was summed so far
         if (!greedy && M > -INFINITY) Z *= exp2_f64(((double)M - (double)q[u].m) * c);
         M = q[u].m;
-        idx = q[u].idx;
-        if (!greedy) Z += (double)q[u].s;
+        idx = partial_idx(q[u]);
+        if (!greedy) Z += (double)s;
       } else if (!greedy && q[u].m > -INFINITY) {
-        Z += (double)q[u].s * exp2_f64(((double)q[u].m - (double)M) * c);
+        Z += (double)s * exp2_f64(((double)q[u].m - (double)M) * c);
       }
     }
   }
-  RowStat r{M, 0.0, idx, !nan && M > -INFINITY && M < INFINITY};
+  RowStat r{M, 0.0, idx, !bad && M > -INFINITY && M < INFINITY};
   if (greedy || !r.ok) return r;
   r.Z = Z;
   r.ok = Z > 0.0 && Z < 1e308;

@@ -136,6 +136,7 @@ __global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
     J.skip = 0ull;
     J.chunk_tiles = 0;
     J.pad = 0;
+    J.slow = 0.0;
     J.trow = t0 + e;
     J.drow = 0;
     J.rho = 0.0;

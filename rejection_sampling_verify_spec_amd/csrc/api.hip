@@ -14,7 +14,7 @@
 
 using namespace sv;
 
-static_assert(sizeof(Partial) == 16, "Partial layout");
+static_assert(sizeof(Partial) == 8, "Partial layout");
 static_assert(sizeof(TileRec) == 128, "TileRec layout");
 
 namespace {
@@ -45,19 +45,21 @@ int nchunk_for(int V, int dt) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workspace layout: row-chunk partials | sampling jobs | tile records.
+// Workspace layout: row-chunk partials | sampling jobs | tile records |
+// per-request counters.
 struct Carve {
-  size_t part, jobs, recs, total;
+  size_t part, jobs, recs, done, total;
 };
 
 Carve carve(long long rows, int B, int V, int dt) {
   Carve c;
   const int nchunk = nchunk_for(V, dt);
-  const int ntile = (V + kSTile - 1) / kSTile;
+  const int ntile = tiles_per_row(V, dt);
   c.part = 0;
   c.jobs = align256((size_t)rows * nchunk * sizeof(Partial));
   c.recs = c.jobs + align256((size_t)B * sizeof(SampleJob));
-  c.total = c.recs + align256((size_t)B * ntile * sizeof(TileRec));
+  c.done = c.recs + align256((size_t)B * ntile * sizeof(TileRec));
+  c.total = c.done + align256((size_t)B * sizeof(int));
   return c;
 }
 
@@ -90,10 +92,26 @@ void timing_mark(hipStream_t st, bool start) {
 }
 
 int launch_stats(int dt, const void* tgt, const void* dft, int V, const Layout& L, const float* temperature,
-                 Partial* part, hipStream_t st) {
+                 Partial* part, hipStream_t st, int* zero_counts = nullptr) {
   timing_mark(st, true);
-  hipError_t e = launch_row_stats(dt, tgt, dft, V, L, temperature, chunk_vecs(), nchunk_for(V, dt), part, st);
+  hipError_t e =
+      launch_row_stats(dt, tgt, dft, V, L, temperature, chunk_vecs(), nchunk_for(V, dt), part, zero_counts, st);
   timing_mark(st, false);
+  return e == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+// The chain kernels (streaming statistics, then one workgroup per request) on a
+// carved workspace.
+int launch_chain(int dt, const void* tgt, const void* dft, int V, const Layout& L, const int32_t* tokens,
+                 const float* ua, const float* us, const float* temperature, int32_t* out, int out_width,
+                 int32_t* num_acc, float* diag, char* ws, const Carve& cv, hipStream_t st) {
+  Partial* part = reinterpret_cast<Partial*>(ws + cv.part);
+  int* done = reinterpret_cast<int*>(ws + cv.done);
+  int rc = launch_stats(dt, tgt, dft, V, L, temperature, part, st, done);
+  if (rc) return rc;
+  hipError_t e = launch_verify_chain(dt, tgt, dft, V, L, tokens, ua, us, temperature, part, nchunk_for(V, dt),
+                                     chunk_vecs(), reinterpret_cast<TileRec*>(ws + cv.recs), done, out, out_width,
+                                     num_acc, diag, force_exact_residual(), st);
   return e == hipSuccess ? SV_OK : SV_EHIP;
 }
 
@@ -152,18 +170,10 @@ int spec_verify(const void* target_logits, const void* draft_logits, int32_t dty
   Carve cv = carve(RT + RD, B, V, dtype);
   rc = check_ws(workspace, workspace_bytes, cv.total);
   if (rc) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  Partial* part = reinterpret_cast<Partial*>(ws + cv.part);
-  SampleJob* jobs = reinterpret_cast<SampleJob*>(ws + cv.jobs);
-  TileRec* recs = reinterpret_cast<TileRec*>(ws + cv.recs);
   Layout L{LAYOUT_DENSE, B, gamma, nullptr, 0, RT, RD};
-  if ((rc = launch_stats(dtype, target_logits, draft_logits, V, L, temperature, part, st))) return rc;
-  if (launch_finish_chain(dtype, target_logits, draft_logits, V, L, draft_tokens, u_accept, u_sample, temperature,
-                          part, nchunk_for(V, dtype), chunk_vecs(), out_tokens, gamma + 1, num_accepted, diag_probs, jobs,
-                          recs, force_exact_residual(), st) != hipSuccess)
-    return SV_EHIP;
-  return SV_OK;
+  return launch_chain(dtype, target_logits, draft_logits, V, L, draft_tokens, u_accept, u_sample, temperature,
+                      out_tokens, gamma + 1, num_accepted, diag_probs, static_cast<char*>(workspace), cv,
+                      static_cast<hipStream_t>(stream));
 }
 
 int spec_verify_ragged(const void* target_logits, const void* draft_logits, int32_t dtype, const int32_t* cu_gamma,
@@ -182,18 +192,10 @@ int spec_verify_ragged(const void* target_logits, const void* draft_logits, int3
   Carve cv = carve(RT + RD, B, V, dtype);
   rc = check_ws(workspace, workspace_bytes, cv.total);
   if (rc) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  Partial* part = reinterpret_cast<Partial*>(ws + cv.part);
-  SampleJob* jobs = reinterpret_cast<SampleJob*>(ws + cv.jobs);
-  TileRec* recs = reinterpret_cast<TileRec*>(ws + cv.recs);
   Layout L{LAYOUT_RAGGED, B, gamma_max, cu_gamma, total_draft, RT, RD};
-  if ((rc = launch_stats(dtype, target_logits, draft_logits, V, L, temperature, part, st))) return rc;
-  if (launch_finish_chain(dtype, target_logits, draft_logits, V, L, draft_tokens, u_accept, u_sample, temperature,
-                          part, nchunk_for(V, dtype), chunk_vecs(), out_tokens, gamma_max + 1, num_accepted, diag_probs, jobs,
-                          recs, force_exact_residual(), st) != hipSuccess)
-    return SV_EHIP;
-  return SV_OK;
+  return launch_chain(dtype, target_logits, draft_logits, V, L, draft_tokens, u_accept, u_sample, temperature,
+                      out_tokens, gamma_max + 1, num_accepted, diag_probs, static_cast<char*>(workspace), cv,
+                      static_cast<hipStream_t>(stream));
 }
 
 int spec_verify_tree(const void* target_logits, const void* draft_logits, int32_t dtype, const int32_t* node_tokens,

@@ -1,16 +1,17 @@
 // sv_internal.h -- shared types and device helpers of libspecverify (gfx950).
 //
-// Pipeline of one verify call (kernels on the caller's stream; a kernel
-// boundary is the only hand-off between workgroups):
-//   1. row_stats : one streaming pass over every logit row that the method
-//                  reads -> per (row, chunk) max / sum of 2^{(x-max)c} (T>0)
-//                  or max / lowest argmax (T==0), fp32, 16-byte loads.
-//   2. accept    : one workgroup per request: merge of the chunk partials in
-//                  fp64, acceptance test per position (or tree node), first
-//                  rejection, greedy outputs, one sampling job per request.
-//   3. tiles     : several workgroups per request: per tile of the residual or
-//                  bonus row, fp32 triage and, where masses matter, fp64 sums.
-//   4. pick      : one workgroup per request: inverse-CDF search (fp64).
+// A verify call runs three stages over the caller's batch:
+//   1. streaming statistics (row_stats.hip, stream.h): one read of every logit
+//      row the method reads -> per (row, chunk) max and sum of 2^{(x-max)c}
+//      (T > 0) or max and lowest argmax (T == 0), in fp32 from 16-byte loads;
+//   2. acceptance: per request, the chunk partials merged in fp64, the test
+//      at every drafted position (or tree node), the first rejection, greedy
+//      outputs and one sampling job;
+//   3. draw: a tile pass over the drawn row(s) (fp32 triage, fp64 where
+//      masses matter) and an inverse-CDF pick in fp64.
+// Chain layouts run stages 2 and 3 in one kernel with a few workgroups per
+// request (verify.hip); token trees run them as separate kernels (accept.hip,
+// finish.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,7 +21,6 @@ namespace sv {
 
 constexpr int kTPB = 256;        // threads per workgroup (4 waves of 64)
 constexpr int kU = 4;            // 16-byte vectors per thread per step
-constexpr int kSTile = 2048;     // tokens per sampling tile (8 per thread)
 constexpr int kGrp = 5;          // groups of undecided residual tokens kept per tile
 constexpr double kLog2e = 1.4426950408889634073599246810019;
 constexpr double kRhoBand = 1e-5;  // relative half-width of the undecided band around rho
@@ -37,13 +37,42 @@ struct Layout {
   long long RT, RD;     // rows of the target and draft arrays
 };
 
-// Partial statistics of one (row, chunk).
+// Partial statistics of one (row, chunk), published as one 64-bit word.
+//   m : chunk maximum (exact value of a logit), -inf if none;
+//   w : T > 0 : bits of s = sum over the chunk of 2^{(x - m) c} (s >= 1 when
+//               m is finite, 0 when m = -inf, NaN when the chunk holds a NaN
+//               or a +inf);
+//       T == 0: lowest index of the maximum + 2 (>= 1), or kGreedyBad when the
+//               chunk holds a NaN or a +inf.
 struct Partial {
-  float m;    // chunk maximum (exact value of a logit), -inf if none
-  float s;    // T>0: sum over the chunk of 2^{(x-m)c}; T==0: 0, or NaN if the chunk holds NaN/+inf
-  int idx;    // T==0: lowest index of the maximum (-1 if none)
-  int flag;   // 1 when written
+  float m;
+  uint32_t w;
 };
+constexpr uint32_t kGreedyBad = 0xffffffffu;
+
+__device__ __forceinline__ Partial sampling_partial(float m, float s) { return Partial{m, __float_as_uint(s)}; }
+__device__ __forceinline__ Partial greedy_partial(float m, int idx, bool bad) {
+  return Partial{m, bad ? kGreedyBad : (uint32_t)(idx + 2)};
+}
+__device__ __forceinline__ float partial_s(const Partial& p) { return __uint_as_float(p.w); }
+__device__ __forceinline__ int partial_idx(const Partial& p) { return p.w == kGreedyBad ? -1 : (int)p.w - 2; }
+// bad for either kind: NaN sum or the greedy flag
+__device__ __forceinline__ bool partial_bad(const Partial& p, bool greedy) {
+  return greedy ? p.w == kGreedyBad : !(partial_s(p) == partial_s(p));
+}
+
+// Partials as 64-bit words (m in the low half, w in the high half: the
+// in-memory order of the struct), written and read as single device-scope
+// accesses.
+__device__ __forceinline__ void publish_partial(Partial* p, Partial v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), ((uint64_t)v.w << 32) | (uint64_t)__float_as_uint(v.m),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ Partial read_partial(const Partial* p) {
+  const uint64_t x = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<Partial*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return Partial{__uint_as_float((uint32_t)x), (uint32_t)(x >> 32)};
+}
 
 enum JobKind : int { JOB_NONE = 0, JOB_BONUS = 1, JOB_RESIDUAL = 2 };
 
@@ -58,9 +87,10 @@ struct SampleJob {
   float mt, md;       // row maxima (exact)
   float u;            // sampling uniform
   float c32;          // fl32(c64): argument of the fp32 exponential for negligible masses
-  unsigned long long skip;  // bonus: row chunks whose tiles are not read (bit k = chunk k)
+  unsigned long long skip;  // row chunks whose tiles are not read (bit k = chunk k)
   int chunk_tiles;    // tiles per chunk when skip != 0
   int pad;
+  double slow;        // residual: a lower bound of the residual total S (units of the target row maximum)
 };
 
 // Per (job, tile) record of the sampling pass (fp64 sums in a fixed order).
@@ -78,6 +108,13 @@ struct TileRec {
   double ged[kGrp];   // per group: sum of e_d
   double pad2;
 };
+
+
+// Tokens per sampling tile: 4 16-byte vectors per lane when one wave owns a
+// tile (2048 bf16 or 1024 fp32 tokens).
+template <int DT> struct TileTok { static constexpr int value = DT == 1 ? 2048 : 1024; };
+__host__ __device__ inline int tile_tokens(int dt) { return dt == 1 ? 2048 : 1024; }
+__host__ __device__ inline int tiles_per_row(int V, int dt) { return (V + tile_tokens(dt) - 1) / tile_tokens(dt); }
 
 // TileRec::ngrp codes.
 constexpr int kRecOverflow = -1;    // undecided tokens did not fit: the pick recomputes the tile
@@ -174,18 +211,14 @@ __device__ __forceinline__ double exp2_f64(double a) {
 // fp32 2^x on the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float exp2_f32(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Mass 2^{(l - m) c} of one token in double precision (c64 = c, c32 = fl32(c)).
-// Terms below 2^-50 of the row maximum (fp32 argument a32 < -50) take the fp32
-// exponential unit: the argument's error (three fp32 roundings, about
-// 2e-7 |a|) and the unit's ulp leave an absolute error below 2^-60 per token,
-// under the rounding of the double-precision sums these terms enter.
+// Masses below 2^-50 of their row maximum (fp32 exponent argument below this)
+// are evaluated on the fp32 exponential unit.
 constexpr float kTinyExp = -50.0f;
-__device__ __forceinline__ double emass(float l, float m, double c64, float c32) {
-  const float a32 = (l - m) * c32;
-  double e = (double)exp2_f32(a32);
-  if (a32 >= kTinyExp) e = exp2_f64(((double)l - (double)m) * c64);
-  return e;
-}
+// Masses below 2^-100 of their row maximum are left out of the draw's tile
+// sums when a whole 16-byte vector of them, in every lane of a wave, lies
+// there: at most V 2^-100 of the row maximum in all, below the double-precision
+// resolution of any CDF position.
+constexpr float kDropExp = -100.0f;
 
 // ---------------------------------------------------------------------------
 // Wave64 / workgroup reductions.
@@ -197,18 +230,65 @@ __device__ __forceinline__ T wave_reduce(T v, F op) {
   return v;
 }
 
+// Wave64 reductions and scans on DPP lane moves (gfx9 controls: row_shr:n =
+// 0x110 + n inside rows of 16 lanes, row_bcast:15 = 0x142 into rows 1 and 3,
+// row_bcast:31 = 0x143 into rows 2 and 3). Every lane of the wave must be
+// active. The association order is fixed, so results are reproducible; the
+// totals are read from lane 63 and are the same in every lane.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)b, CTRL, ROW_MASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), CTRL, ROW_MASK, 0xf, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+// Inclusive prefix sum over the 64 lanes (lanes without a source add +0).
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  v += dpp_f64<0x111, 0xf>(v);
+  v += dpp_f64<0x112, 0xf>(v);
+  v += dpp_f64<0x114, 0xf>(v);
+  v += dpp_f64<0x118, 0xf>(v);
+  v += dpp_f64<0x142, 0xa>(v);
+  v += dpp_f64<0x143, 0xc>(v);
+  return v;
+}
+
+__device__ __forceinline__ double lane_f64(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, lane), hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Sum over the wave, the same value in every lane.
+__device__ __forceinline__ double wave_sum(double v) { return lane_f64(wave_incl_scan(v), 63); }
+
+// min / max of an int over the wave.
+template <bool MAX>
+__device__ __forceinline__ int wave_minmax(int v) {
+  constexpr int id = MAX ? (int)0x80000000 : 0x7fffffff;
+  auto op = [](int a, int b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x111, 0xf, 0xf, false));
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x112, 0xf, 0xf, false));
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x114, 0xf, 0xf, false));
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x118, 0xf, 0xf, false));
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x142, 0xa, 0xf, false));
+  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 // Host-side launchers (defined next to their kernels).
 hipError_t launch_row_stats(int dt, const void* tgt, const void* dft, int V, const Layout& L,
-                            const float* temperature, int chunk_vecs, int nchunk, Partial* part,
+                            const float* temperature, int chunk_vecs, int nchunk, Partial* part, int* zero_counts,
                             hipStream_t st);
 hipError_t launch_accept_tree(int dt, const void* tgt, const void* dft, int V, const Layout& L, int max_depth,
                               const int32_t* tokens, const int32_t* parents, const float* ua, const float* us,
                               const float* temperature, const Partial* part, int nchunk, int32_t* out,
                               int32_t* out_nodes, int32_t* num_acc, SampleJob* jobs, hipStream_t st);
-hipError_t launch_finish_chain(int dt, const void* tgt, const void* dft, int V, const Layout& L,
+hipError_t launch_verify_chain(int dt, const void* tgt, const void* dft, int V, const Layout& L,
                                const int32_t* tokens, const float* ua, const float* us, const float* temperature,
-                               const Partial* part, int nchunk, int chunk_vecs, int32_t* out, int out_width,
-                               int32_t* num_acc, float* diag, SampleJob* jobs, TileRec* recs, int force_exact,
+                               const Partial* part, int nchunk, int chunk_vecs, TileRec* recs, int* done,
+                               int32_t* out, int out_width, int32_t* num_acc, float* diag, int force_exact,
                                hipStream_t st);
 hipError_t launch_finish_jobs(int dt, const void* tgt, const void* dft, int V, int B, SampleJob* jobs,
                               TileRec* recs, int32_t* out, int out_width, int force_exact, hipStream_t st);

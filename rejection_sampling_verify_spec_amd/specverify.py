@@ -16,7 +16,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+# the in-tree build; SPECVERIFY_LIB names another build of the same library
+LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(_HERE, "libspecverify.so")
 
 SV_OK, SV_EINVAL, SV_EDTYPE, SV_ENOWS, SV_EALIGN, SV_EHIP = 0, -1, -2, -3, -4, -5
 SV_F32, SV_BF16 = 0, 1
