@@ -47,7 +47,7 @@ namespace sv {
 constexpr int kList = 64;             // undecided tokens collected per tile
 constexpr int kSparse = 3;            // live tokens per lane up to which a tile skips the fp32 triage
 constexpr int kMaxPos = SV_MAX_GAMMA + 1;
-constexpr int kRowLanes = 8;          // lanes merging one row's chunk partials
+constexpr int kRowLanes = 8;          // lanes merging one row's chunk partials (DPP groups of 8)
 
 template <int DT, int NW> struct TileGeom {
   static constexpr int nt = NW * 64;                       // threads of the workgroup
@@ -233,13 +233,17 @@ __device__ __forceinline__ void merge_row_group(Src src, int nchunk, double c, b
     bad |= partial_bad(q, greedy);
     if (q.m > M) { M = q.m; idx = partial_idx(q); }
   }
-#pragma unroll
-  for (int off = 1; off < kRowLanes; off <<= 1) {
-    const float M2 = __shfl_xor(M, off, 64);
-    const int i2 = __shfl_xor(idx, off, 64);
-    bad |= __shfl_xor((int)bad, off, 64) != 0;
+  // exchanges inside the group of 8 lanes: xor 1 and xor 2 (quad permutes),
+  // then the mirrored lane of the other quad
+  auto step = [&](auto mv) {
+    const float M2 = __int_as_float(mv(__float_as_int(M)));
+    const int i2 = mv(idx);
+    bad |= mv((int)bad) != 0;
     if (M2 > M || (M2 == M && (unsigned)i2 < (unsigned)idx)) { M = M2; idx = i2; }
-  }
+  };
+  step([](int v) { return __builtin_amdgcn_update_dpp(0, v, 0xb1, 0xf, 0xf, false); });
+  step([](int v) { return __builtin_amdgcn_update_dpp(0, v, 0x4e, 0xf, 0xf, false); });
+  step([](int v) { return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false); });
   ok = !bad && M > -INFINITY && M < INFINITY;
   Z = 0.0;
   if (greedy || !ok) return;
@@ -247,8 +251,9 @@ __device__ __forceinline__ void merge_row_group(Src src, int nchunk, double c, b
     const Partial q = src(k);
     if (q.m > -INFINITY) Z += (double)partial_s(q) * exp2_f64(((double)q.m - (double)M) * c);
   }
-#pragma unroll
-  for (int off = 1; off < kRowLanes; off <<= 1) Z += __shfl_xor(Z, off, 64);
+  Z += dpp_f64<0xb1, 0xf>(Z);
+  Z += dpp_f64<0x4e, 0xf>(Z);
+  Z += dpp_f64<0x141, 0xf>(Z);
   ok = Z > 0.0 && Z < 1e308;
 }
 
@@ -337,7 +342,6 @@ __device__ __forceinline__ void find_skipped_chunks(const void* tgt, const void*
     if (res) mass_d[lane] = md;
   }
   if (res) {
-    auto add = [](double a, double b) { return a + b; };
     const double dropped = wave_sum(tiny ? mt : 0.0);
     const double dtv = mt - J.rho * md, tv_margin = 2e-6 * (mt + J.rho * md);
     const double tv = wave_sum(lane < nchunk ? fmax(0.0, fabs(dtv) - tv_margin) : 0.0);
@@ -906,9 +910,17 @@ __device__ __forceinline__ double block_sum(double v, double* red) {
 template <int DT, int NW>
 __device__ __forceinline__ void load_tile_block(const char* rowp, int j0, int V, float* x) {
   constexpr int bt = TileGeom<DT, NW>::bt;
+  constexpr int es = sizeof(typename Elem<DT>::T);
+  const int jt = j0 + bt * (int)threadIdx.x;
+  const char* p = rowp + (size_t)jt * es;
+  if (bt * es == 16 && jt + bt <= V && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+    // the thread's tokens are one aligned 16-byte vector
+    unpack<DT>(*reinterpret_cast<const uint4*>(p), x);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < bt; ++i) {
-    const int j = j0 + bt * (int)threadIdx.x + i;
+    const int j = jt + i;
     x[i] = j < V ? Elem<DT>::at(rowp, j) : -INFINITY;
   }
 }
@@ -921,7 +933,6 @@ __device__ __forceinline__ void pick_impl(const char* trow, const char* drow, in
   constexpr int tok = TileGeom<DT, NW>::tok;
   constexpr int bt = TileGeom<DT, NW>::bt;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  auto add = [](double a, double b) { return a + b; };
   // the records, copied into LDS in one pass when they fit
   constexpr bool staged = STAGED;
   if (staged) {
@@ -932,7 +943,60 @@ __device__ __forceinline__ void pick_impl(const char* trow, const char* drow, in
   auto rw = [&](int k, int w) -> uint64_t { return staged ? P.rw[k * kRecWords + w] : rec_load(R + k, w); };
   auto rf = [&](int k, int w) -> double { return __longlong_as_double((long long)rw(k, w)); };
   auto rng = [&](int k) -> int { return (int)(uint32_t)rw(k, kRecNgrp); };
-  // --- exact normalisers: wave 0, lanes over tiles, fixed-order sums
+  // --- tile masses, total S, and the first tile whose inclusive prefix exceeds
+  // u S (wave 0; rho = Z_t / Z_d for a residual)
+  auto tile_mass = [&](int k, bool r, double rho) -> double {
+    if (!r) return rf(k, kRecZt);
+    const int ng = rng(k);
+    if (ng == kRecRecomputed) return rf(k, kRecZd);
+    double t = rf(k, kRecDpos) + (J.rho - rho) * rf(k, kRecBpos);
+    for (int g = 0; g < ng; ++g) {
+      const double q = rf(k, kRecGet + g) - rho * rf(k, kRecGed + g);
+      t += q > 0.0 ? q : 0.0;
+    }
+    return t > 0.0 ? t : 0.0;
+  };
+  auto scan_tiles = [&](bool res, double rho) {
+    // the tile masses, one per lane and 64-tile round, kept for the scan
+    double part = 0.0;
+    for (int k = lane; k < ntile; k += 64) part += tile_mass(k, res, rho);
+    double S = wave_sum(part);
+    if (!(S > 0.0) && res) {  // residual underflow: draw from p_t of the same row
+      res = false;
+      part = 0.0;
+      for (int k = lane; k < ntile; k += 64) part += tile_mass(k, false, rho);
+      S = wave_sum(part);
+    }
+    const double thr = (double)J.u * S;
+    double base = 0.0;
+    int tile = -1, lastpos = -1;
+    double W = 0.0;
+    for (int k0 = 0; k0 < ntile; k0 += 64) {
+      const int k = k0 + lane;
+      const double t = k < ntile ? tile_mass(k, res, rho) : 0.0;
+      const double incl = wave_incl_scan(t);
+      const unsigned long long pos = __ballot(t > 0.0);
+      if (pos) lastpos = k0 + 63 - __builtin_clzll(pos);
+      const unsigned long long hit = __ballot(t > 0.0 && base + incl > thr);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        tile = k0 + l;
+        W = base + lane_f64(incl - t, l);
+        break;
+      }
+      base += lane_f64(incl, 63);
+    }
+    if (lane == 0) {
+      P.last_mode = tile < 0;  // rounding left no tile above u S: last token with positive mass
+      P.tile = tile < 0 ? lastpos : tile;
+      P.W = W;
+      P.thr = thr;
+      P.res = res;
+    }
+  };
+
+  // --- exact normalisers (wave 0, lanes over tiles, fixed-order sums); the
+  // scan follows in the same wave unless tiles must first be recomputed
   if (wv == 0) {
     double zt = 0.0, zd = 0.0;
     int need = 0;
@@ -944,22 +1008,23 @@ __device__ __forceinline__ void pick_impl(const char* trow, const char* drow, in
     zt = wave_sum(zt);
     zd = wave_sum(zd);
     need = __any(need);
+    const bool res = J.kind == JOB_RESIDUAL;
+    const double rho = res ? zt / zd : 0.0;
+    // every token outside the band has the same residual sign under rho and rho~
+    const bool exact_all = res && (force_exact || !(fabs(rho - J.rho) <= 0.5 * kRhoBand * J.rho));
+    const int any_exact = res && (exact_all || need) ? (exact_all ? 2 : 1) : 0;
     if (lane == 0) {
-      const bool res = J.kind == JOB_RESIDUAL;
-      const double rho = res ? zt / zd : 0.0;
       P.Zt = zt;
       P.Zd = zd;
-      P.res = res;
-      // every token outside the band has the same residual sign under rho and rho~
-      const bool exact_all = res && (force_exact || !(fabs(rho - J.rho) <= 0.5 * kRhoBand * J.rho));
-      P.any_exact = res && (exact_all || need) ? (exact_all ? 2 : 1) : 0;
+      P.any_exact = any_exact;
     }
+    if (!any_exact) scan_tiles(res, rho);
   }
   __syncthreads();
-  bool res = P.res != 0;
-  const double rho = res ? P.Zt / P.Zd : 0.0;
+  const double rho = J.kind == JOB_RESIDUAL ? P.Zt / P.Zd : 0.0;
 
-  // --- tiles whose residual mass is recomputed token by token (then marked kRecRecomputed, mass in zd)
+  // --- tiles whose residual mass is recomputed token by token (then marked
+  // kRecRecomputed, mass in zd), and the scan
   if (P.any_exact) {
     const bool all = P.any_exact == 2;
     for (int k = 0; k < ntile; ++k) {
@@ -986,60 +1051,10 @@ __device__ __forceinline__ void pick_impl(const char* trow, const char* drow, in
       __builtin_amdgcn_s_waitcnt(0);  // the stores are complete before any wave reads them back
       __syncthreads();
     }
+    if (wv == 0) scan_tiles(true, rho);
+    __syncthreads();
   }
-
-  // --- tile masses, total S, and the first tile whose inclusive prefix exceeds u S (wave 0)
-  auto tile_mass = [&](int k, bool r) -> double {
-    if (!r) return rf(k, kRecZt);
-    const int ng = rng(k);
-    if (ng == kRecRecomputed) return rf(k, kRecZd);
-    double t = rf(k, kRecDpos) + (J.rho - rho) * rf(k, kRecBpos);
-    for (int g = 0; g < ng; ++g) {
-      const double q = rf(k, kRecGet + g) - rho * rf(k, kRecGed + g);
-      t += q > 0.0 ? q : 0.0;
-    }
-    return t > 0.0 ? t : 0.0;
-  };
-  if (wv == 0) {
-    // the tile masses, one per lane and 64-tile round, kept for the scan
-    double part = 0.0;
-    for (int k = lane; k < ntile; k += 64) part += tile_mass(k, res);
-    double S = wave_sum(part);
-    if (!(S > 0.0) && res) {  // residual underflow: draw from p_t of the same row
-      res = false;
-      part = 0.0;
-      for (int k = lane; k < ntile; k += 64) part += tile_mass(k, false);
-      S = wave_sum(part);
-    }
-    const double thr = (double)J.u * S;
-    double base = 0.0;
-    int tile = -1, lastpos = -1;
-    double W = 0.0;
-    for (int k0 = 0; k0 < ntile; k0 += 64) {
-      const int k = k0 + lane;
-      const double t = k < ntile ? tile_mass(k, res) : 0.0;
-      const double incl = wave_incl_scan(t);
-      const unsigned long long pos = __ballot(t > 0.0);
-      if (pos) lastpos = k0 + 63 - __builtin_clzll(pos);
-      const unsigned long long hit = __ballot(t > 0.0 && base + incl > thr);
-      if (hit) {
-        const int l = __builtin_ctzll(hit);
-        tile = k0 + l;
-        W = base + lane_f64(incl - t, l);
-        break;
-      }
-      base += lane_f64(incl, 63);
-    }
-    if (lane == 0) {
-      P.last_mode = tile < 0;  // rounding left no tile above u S: last token with positive mass
-      P.tile = tile < 0 ? lastpos : tile;
-      P.W = W;
-      P.thr = thr;
-      P.res = res;
-    }
-  }
-  __syncthreads();
-  res = P.res != 0;
+  const bool res = P.res != 0;
   const int tile = P.tile;
   if (tile < 0) {  // no positive mass anywhere (cannot happen for usable rows)
     if (tid == 0) *dst = -1;
