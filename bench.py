@@ -35,6 +35,7 @@ HBM_PEAK_GBPS = 8000.0
 KERNEL = "k_row_stats"
 PMC_FILE = os.path.join(ROOT, "profiles", "row_stats_large_pmc.json")
 KERNEL_SOURCES = ["rejection_sampling_verify_spec_amd/csrc/row_stats.hip",
+                  "rejection_sampling_verify_spec_amd/csrc/stream.h",
                   "rejection_sampling_verify_spec_amd/csrc/sv_internal.h"]
 
 WORKLOAD_TEXT = {
@@ -355,11 +356,11 @@ def summarize_rocprof(path):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="large", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
-    ap.add_argument("--time-every", type=int, default=8,
+    ap.add_argument("--time-every", type=int, default=16,
                     help="record the row-statistics kernel's HIP events on every N-th timed step")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall time spent timing the CPU oracle")
     ap.add_argument("--skip-cpu-baseline", action="store_true", help="no oracle run (profiling runs)")

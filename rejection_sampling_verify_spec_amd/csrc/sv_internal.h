@@ -230,53 +230,6 @@ __device__ __forceinline__ T wave_reduce(T v, F op) {
   return v;
 }
 
-// Wave64 reductions and scans on DPP lane moves (gfx9 controls: row_shr:n =
-// 0x110 + n inside rows of 16 lanes, row_bcast:15 = 0x142 into rows 1 and 3,
-// row_bcast:31 = 0x143 into rows 2 and 3). Every lane of the wave must be
-// active. The association order is fixed, so results are reproducible; the
-// totals are read from lane 63 and are the same in every lane.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)b, CTRL, ROW_MASK, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), CTRL, ROW_MASK, 0xf, false);
-  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
-}
-
-// Inclusive prefix sum over the 64 lanes (lanes without a source add +0).
-__device__ __forceinline__ double wave_incl_scan(double v) {
-  v += dpp_f64<0x111, 0xf>(v);
-  v += dpp_f64<0x112, 0xf>(v);
-  v += dpp_f64<0x114, 0xf>(v);
-  v += dpp_f64<0x118, 0xf>(v);
-  v += dpp_f64<0x142, 0xa>(v);
-  v += dpp_f64<0x143, 0xc>(v);
-  return v;
-}
-
-__device__ __forceinline__ double lane_f64(double v, int lane) {
-  const long long b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_readlane((int)b, lane), hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
-}
-
-// Sum over the wave, the same value in every lane.
-__device__ __forceinline__ double wave_sum(double v) { return lane_f64(wave_incl_scan(v), 63); }
-
-// min / max of an int over the wave.
-template <bool MAX>
-__device__ __forceinline__ int wave_minmax(int v) {
-  constexpr int id = MAX ? (int)0x80000000 : 0x7fffffff;
-  auto op = [](int a, int b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
-  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x111, 0xf, 0xf, false));
-  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x112, 0xf, 0xf, false));
-  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x114, 0xf, 0xf, false));
-  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x118, 0xf, 0xf, false));
-  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x142, 0xa, 0xf, false));
-  v = op(v, __builtin_amdgcn_update_dpp(id, v, 0x143, 0xc, 0xf, false));
-  return __builtin_amdgcn_readlane(v, 63);
-}
-
 // Host-side launchers (defined next to their kernels).
 hipError_t launch_row_stats(int dt, const void* tgt, const void* dft, int V, const Layout& L,
                             const float* temperature, int chunk_vecs, int nchunk, Partial* part, int* zero_counts,
