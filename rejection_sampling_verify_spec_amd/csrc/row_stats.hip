@@ -1,6 +1,5 @@
-// row_stats.hip -- the streaming row-statistics kernel as a launch of its own
-// (token trees and the statistics entry point; chain layouts run the same
-// device code inside the persistent verify kernel), and the per-row
+// row_stats.hip -- the streaming row-statistics kernel (the first launch of
+// every verify call and of the statistics entry point), and the per-row
 // finalisation of the statistics entry point.
 #include "stream.h"
 

@@ -1,6 +1,5 @@
 // stream.h -- per-(row, chunk) softmax statistics, the HBM-bound streaming
-// pass of a verify call (device code shared by the row-statistics kernel and
-// the persistent verify kernel).
+// pass of a verify call (device code of the row-statistics kernel).
 //
 // One workgroup computes, in one read of its chunk:
 //   T > 0 : m = max x and s = sum 2^{(x - m) c} with c = log2(e)/T, i.e. the

@@ -1,5 +1,5 @@
 // tail.h -- the tail of a verify call after the streaming pass (device code
-// shared by the persistent verify kernel and the token-tree kernels):
+// shared by the chain tail kernel and the token-tree kernels):
 // the acceptance scan of a chain request and the draw of a request's final
 // token.
 //
@@ -18,7 +18,9 @@
 // q_j = max(0, e_t(j) - rho e_d(j)) with rho = Z_t / Z_d, so that the chosen
 // token agrees with a double-precision sequential evaluation unless u S lies
 // within ~1e-13 S of a CDF boundary.
-//   tile pass (one wave per tile of 2048 bf16 / 1024 fp32 tokens): an fp32
+//   tile pass (one wave per tile of 2048 bf16 / 1024 fp32 tokens): tokens
+//   below 2^-100 of the row maximum in both rows are left out; when few
+//   remain they go straight to double precision, else through an fp32
 //   triage; tokens whose masses are negligible (below 2^-50 of the row
 //   maximum) and, for a residual, whose likelihood ratios are clear of the band
 //   around the estimate rho~ (from the fp32 row statistics) are summed in fp32;
@@ -33,10 +35,10 @@
 //   token), a scan over tiles for the one holding u S, and a fixed-order fp64
 //   scan of that tile.
 //
-// A chain request's tail runs in one workgroup of NW waves: the acceptance
-// scan, the tile pass (waves take tiles in turn) and the pick, with barriers
-// as the only hand-off. Token trees run the same tile pass and pick as
-// kernels of their own after the tree acceptance kernel.
+// A chain request's tail runs in a few workgroups of NW waves: each runs the
+// acceptance scan, the waves of all of them take the tiles in turn, and the
+// last workgroup to finish runs the pick. Token trees run the same tile pass
+// and pick as kernels of their own after the tree acceptance kernel.
 #pragma once
 
 #include "specverify.h"
