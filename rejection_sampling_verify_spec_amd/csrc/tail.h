@@ -94,7 +94,7 @@ __device__ __forceinline__ int wave_minmax(int v) {
 }
 
 constexpr int kList = 64;             // undecided tokens collected per tile
-constexpr int kSparse = 3;            // live tokens per lane up to which a tile skips the fp32 triage
+constexpr int kSparse = 4;            // live tokens per lane up to which a tile triages them one by one
 constexpr int kMaxPos = SV_MAX_GAMMA + 1;
 constexpr int kRowLanes = 8;          // lanes merging one row's chunk partials (DPP groups of 8)
 
@@ -701,14 +701,31 @@ __device__ __forceinline__ float staged_at(const uint4& v, int e) {
   }
 }
 
+// Token i (u = i / epv, e = i % epv) of a lane's four 16-byte vectors, by
+// selects on the registers (a lane-dependent index).
+template <int DT>
+__device__ __forceinline__ float token_at(uint4 w0, uint4 w1, uint4 w2, uint4 w3, int i) {
+  constexpr int epv = Elem<DT>::kPerVec;
+  const int u = i / epv, e = i % epv;
+  const uint4 v = u == 0 ? w0 : u == 1 ? w1 : u == 2 ? w2 : w3;
+  if constexpr (DT == 1) {
+    const int q = e >> 1;
+    const uint32_t d = q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+    return __uint_as_float((e & 1) ? (d & 0xffff0000u) : (d << 16));
+  } else {
+    const uint32_t d = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+    return __uint_as_float(d);
+  }
+}
+
 // Pass over one tile by one wave; writes the tile record. The lane holds the
 // tile's 16-byte vectors u*64 + lane (u < 4) in wt (and wd); its token (u, e)
 // is token j0 + (u*64 + lane)*epv + e.
 //
 // Tokens below 2^kDropExp of the row maximum in both rows are left out (masses
 // below the resolution of the sums). When no lane holds more than kSparse
-// of the others, they all go to the double-precision step directly. Otherwise
-// every token of a vector holding one first goes through fp32. A token whose mass is below 2^-50 of its
+// of the others, each is picked from the registers and goes through fp32 on
+// its own. Otherwise every token of a vector holding one goes through fp32. A token whose mass is below 2^-50 of its
 // row maximum in both rows (fp32 argument a < kTinyExp) and, for a residual,
 // whose likelihood ratio lies outside twice the band around rho~ contributes
 // terms whose fp32 rounding is below 2^-70 of the row maximum: it is summed,
@@ -757,14 +774,47 @@ __device__ __forceinline__ void tile_pass(uint4 (&wt)[4], uint4 (&wd)[4], const 
     }
     __builtin_amdgcn_sched_barrier(0);  // one vector at a time (register pressure)
   }
+  // fp32 triage of one token (bit `bit` of the lane's flags); a token of -inf
+  // in both rows adds nothing and is not flagged
+  const float rho32 = (float)J.rho;
+  const float hi32 = (float)(J.rho * (1.0 + 2.0 * kRhoBand)), lo32 = (float)(J.rho * (1.0 - 2.0 * kRhoBand));
+  auto triage = [&](float xt, float xd, int bit) {
+    const float at = (xt - mt) * c32;
+    const float et = exp2_f32(at);
+    bool flag = at >= kTinyExp;
+    // selects rather than branches: the sums take a term or +0
+    if (RES) {
+      const float ad = (xd - md) * c32;
+      const float ed = exp2_f32(ad);
+      flag |= ad >= kTinyExp;
+      const bool pos = et > hi32 * ed;
+      flag |= !pos && et > 0.f && et >= lo32 * ed;
+      const bool take_pos = pos && !flag;
+      st += flag ? 0.f : et;
+      sd += flag ? 0.f : ed;
+      sdp += take_pos ? et - rho32 * ed : 0.f;
+      sbp += take_pos ? ed : 0.f;
+    } else {
+      st += flag ? 0.f : et;
+    }
+    flags |= (uint32_t)flag << bit;
+  };
   if (!__any(__builtin_popcount(live) > kSparse)) {
-    // few live tokens per lane (rows whose mass sits on a handful of
-    // tokens): each goes straight to double precision
-    flags = live;
+    // few live tokens per lane (rows whose mass sits on a handful of tokens):
+    // each is taken from the registers by its index and triaged alone
+    uint32_t rest = live;
+#pragma unroll 1
+    while (__any(rest != 0u)) {
+      const bool has = rest != 0u;
+      const int i = has ? __builtin_ctz(rest) : 0;
+      rest &= rest - 1u;
+      float xt = token_at<DT>(wt[0], wt[1], wt[2], wt[3], i);
+      float xd = RES ? token_at<DT>(wd[0], wd[1], wd[2], wd[3], i) : 0.f;
+      if (!has) xt = xd = -INFINITY;
+      triage(xt, xd, i);
+    }
   } else {
-    // fp32 triage of the live vectors
-    const float rho32 = (float)J.rho;
-    const float hi32 = (float)(J.rho * (1.0 + 2.0 * kRhoBand)), lo32 = (float)(J.rho * (1.0 - 2.0 * kRhoBand));
+    // fp32 triage of every token of the live vectors
 #pragma unroll
     for (int u = 0; u < nv; ++u) {
       if (!__any(((live >> (u * epv)) & ((1u << epv) - 1u)) != 0u)) continue;
@@ -776,27 +826,7 @@ __device__ __forceinline__ void tile_pass(uint4 (&wt)[4], uint4 (&wd)[4], const 
       unpack<DT>(t4, xt);
       if (RES) unpack<DT>(d4, xd);
 #pragma unroll
-      for (int e = 0; e < epv; ++e) {
-        const float at = (xt[e] - mt) * c32;
-        const float et = exp2_f32(at);
-        bool flag = at >= kTinyExp;
-        // selects rather than branches: the sums take a term or +0
-        if (RES) {
-          const float ad = (xd[e] - md) * c32;
-          const float ed = exp2_f32(ad);
-          flag |= ad >= kTinyExp;
-          const bool pos = et > hi32 * ed;
-          flag |= !pos && et > 0.f && et >= lo32 * ed;
-          const bool take_pos = pos && !flag;
-          st += flag ? 0.f : et;
-          sd += flag ? 0.f : ed;
-          sdp += take_pos ? et - rho32 * ed : 0.f;
-          sbp += take_pos ? ed : 0.f;
-        } else {
-          st += flag ? 0.f : et;
-        }
-        flags |= (uint32_t)flag << (u * epv + e);
-      }
+      for (int e = 0; e < epv; ++e) triage(xt[e], RES ? xd[e] : 0.f, u * epv + e);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
