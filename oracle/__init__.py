@@ -51,6 +51,8 @@ def _load():
         lib.oracle_verify_tree.restype = I
         lib.oracle_row_stats.argtypes = [P, I, I, I, P, P, P, P, P, I]
         lib.oracle_row_stats.restype = I
+        lib.oracle_sample_rows.argtypes = [P, I, I, I, P, P, P, P, I]
+        lib.oracle_sample_rows.restype = I
         _lib = lib
     return _lib
 
@@ -158,3 +160,23 @@ def row_stats(logits, temperature, nthreads=None):
     if rc != 0:
         raise RuntimeError("oracle_row_stats failed")
     return dict(max=m, logz=lz, argmax=am, valid=valid.astype(bool))
+
+
+def sample_rows(logits, temperature, u, nthreads=None):
+    """One token per row from softmax(l/T) by the inverse-CDF rule (T == 0: lowest argmax).
+
+    Returns tokens (int32, -1 for unusable rows) and the CDF margin (distance of u*S to the
+    nearer edge of the chosen token's interval, over S; NaN for greedy and unusable rows).
+    """
+    logits, dt = _logits(logits)
+    V = logits.shape[-1]
+    rows = logits.size // V
+    temperature = np.ascontiguousarray(np.broadcast_to(np.asarray(temperature, np.float32), (rows,)))
+    u = np.ascontiguousarray(np.broadcast_to(np.asarray(u, np.float32), (rows,)))
+    out = np.empty(rows, np.int32)
+    margin = np.empty(rows, np.float64)
+    rc = _load().oracle_sample_rows(_ptr(logits), dt, rows, V, _ptr(temperature), _ptr(u), _ptr(out),
+                                    _ptr(margin), _threads(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_sample_rows failed")
+    return dict(tokens=out, margin=margin)

@@ -677,4 +677,51 @@ int oracle_row_stats(const void *logits, int dtype, int rows, int V, const float
     return run_parallel(rows, nthreads, (size_t)V, stats_task, &sb);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Draft-token sampling: one token per row from p = softmax(l/T) [Edge,
+ * scheduler section: the temperature softmax both models use], the way the
+ * draft model proposes the tokens that verification then tests [Primer 考点1:
+ * the draft model generates the gamma tokens one by one].  The draw is the
+ * verify draw's inverse CDF, y = min{ j : C_j > u*S } over p in ascending
+ * token order; T == 0 takes the lowest-index argmax.  A row whose
+ * temperature, uniform (T > 0) or logits are unusable gives -1.  margin[r]
+ * is the distance of u*S to the nearer edge of y's interval over S (NaN for
+ * greedy and unusable rows).                                                */
+
+typedef struct {
+    const void *logits;
+    int dtype, V;
+    const float *temperature, *u;
+    int32_t *out;
+    double *margin;
+} sample_batch;
+
+static void sample_task(void *p, int row, double *work)
+{
+    const sample_batch *sb = (const sample_batch *)p;
+    size_t off = (size_t)row * sb->V;
+    float T = sb->temperature[row];
+    sb->out[row] = -1;
+    sb->margin[row] = NAN;
+    if (!temperature_usable(T) || !row_usable(sb->logits, sb->dtype, off, sb->V))
+        return;
+    if (T == 0.0f) {
+        sb->out[row] = argmax_row(sb->logits, sb->dtype, off, sb->V);
+        return;
+    }
+    if (!uniform_usable(sb->u[row]))
+        return;
+    softmax_row(sb->logits, sb->dtype, off, sb->V, (double)T, work, NULL, NULL);
+    sb->out[row] = inverse_cdf(work, sb->V, (double)sb->u[row], &sb->margin[row]);
+}
+
+int oracle_sample_rows(const void *logits, int dtype, int rows, int V, const float *temperature, const float *u,
+                       int32_t *out, double *margin, int nthreads)
+{
+    if (rows < 0 || V < 1 || (dtype != OR_F32 && dtype != OR_BF16))
+        return -1;
+    sample_batch sb = {logits, dtype, V, temperature, u, out, margin};
+    return run_parallel(rows, nthreads, (size_t)V, sample_task, &sb);
+}
+
 int oracle_version(void) { return 1; }
