@@ -172,6 +172,35 @@ int spec_row_softmax_stats(const void* logits, int32_t dtype, int32_t rows, int3
                            const float* temperature, float* out_max, float* out_logz, int32_t* out_argmax,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes for spec_sample_rows. */
+size_t spec_sample_rows_workspace_bytes(int32_t rows, int32_t V, int32_t dtype);
+
+/*
+ * Draft-token sampling: one token per logit row, drawn from
+ * p = softmax(l/T) [Edge scheduler section: the temperature softmax
+ * exp((l - max)/T) / sum], the way the draft model proposes the tokens that
+ * verification then tests [Primer 考点1]. The draw is the inverse CDF of the
+ * verify draw: y = min{ j : C_j > u*S } in ascending token order, C the
+ * running sum of p (zero-mass tokens are never drawn; if rounding leaves no
+ * such j, the last token of positive mass). T == 0 takes the lowest index of
+ * the maximum and ignores u.
+ *   logits      [rows, V] (dtype SV_F32 or SV_BF16), row-major
+ *   temperature [rows] float
+ *   u           [rows] float, the caller's uniforms in [0, 1)
+ *   out_tokens  [rows] int32: the drawn token, or -1 for an unusable row
+ *               (temperature NaN, negative, infinite or subnormal; for T > 0 a
+ *               uniform NaN or outside [0, 1); a row holding a NaN, a +inf or
+ *               no finite value)
+ * All pointers are device pointers owned by the caller; the call is
+ * asynchronous on `stream` and allocates nothing (scratch is `workspace`,
+ * 256-byte aligned, at least spec_sample_rows_workspace_bytes). Returns
+ * SV_EINVAL (rows < 0, a null pointer, V out of range), SV_EDTYPE, SV_EALIGN
+ * (logits not aligned to their element size), SV_ENOWS or SV_EHIP before or
+ * at launch; nothing is enqueued on a host-side error.
+ */
+int spec_sample_rows(const void* logits, int32_t dtype, int32_t rows, int32_t V, const float* temperature,
+                     const float* u, int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable text for an sv_status. */
 const char* spec_verify_strerror(int status);
 

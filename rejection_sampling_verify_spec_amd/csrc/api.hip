@@ -138,6 +138,11 @@ size_t spec_verify_tree_workspace_bytes(int32_t B, int32_t N, int32_t V, int32_t
   return carve((long long)B * (2 * N - 1), B, V, dtype).total;
 }
 
+size_t spec_sample_rows_workspace_bytes(int32_t rows, int32_t V, int32_t dtype) {
+  if (rows < 0 || V < 1 || V > SV_MAX_VOCAB || (dtype != 0 && dtype != 1)) return 0;
+  return carve(rows, rows, V, dtype).total;
+}
+
 size_t spec_row_softmax_stats_workspace_bytes(int32_t rows, int32_t V, int32_t dtype) {
   if (rows < 0 || V < 1 || V > SV_MAX_VOCAB || (dtype != 0 && dtype != 1)) return 0;
   return align256((size_t)rows * nchunk_for(V, dtype) * sizeof(Partial));
@@ -245,6 +250,31 @@ int spec_row_softmax_stats(const void* logits, int32_t dtype, int32_t rows, int3
   Layout L{LAYOUT_ROWS, rows, 0, nullptr, 0, rows, 0};
   if ((rc = launch_stats(dtype, logits, nullptr, V, L, temperature, part, st))) return rc;
   if (launch_stats_finalize(part, nchunk_for(V, dtype), rows, temperature, out_max, out_logz, out_argmax, st) !=
+      hipSuccess)
+    return SV_EHIP;
+  return SV_OK;
+}
+
+int spec_sample_rows(const void* logits, int32_t dtype, int32_t rows, int32_t V, const float* temperature,
+                     const float* u, int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows < 0) return SV_EINVAL;
+  if (rows == 0) return SV_OK;
+  int rc = check_common(logits, nullptr, false, dtype, V);
+  if (rc) return rc;
+  if (!temperature || !u || !out_tokens) return SV_EINVAL;
+  Carve cv = carve(rows, rows, V, dtype);
+  rc = check_ws(workspace, workspace_bytes, cv.total);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  Partial* part = reinterpret_cast<Partial*>(ws + cv.part);
+  SampleJob* jobs = reinterpret_cast<SampleJob*>(ws + cv.jobs);
+  TileRec* recs = reinterpret_cast<TileRec*>(ws + cv.recs);
+  Layout L{LAYOUT_ROWS, rows, 0, nullptr, 0, rows, 0};
+  if ((rc = launch_stats(dtype, logits, nullptr, V, L, temperature, part, st))) return rc;
+  if (launch_sample_jobs(part, nchunk_for(V, dtype), rows, temperature, u, jobs, out_tokens, st) != hipSuccess)
+    return SV_EHIP;
+  if (launch_finish_jobs(dtype, logits, logits, V, rows, jobs, recs, out_tokens, 1, force_exact_residual(), st) !=
       hipSuccess)
     return SV_EHIP;
   return SV_OK;

@@ -46,6 +46,10 @@ _lib.spec_verify_tree.argtypes = [_P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I32, 
 _lib.spec_verify_tree.restype = ctypes.c_int
 _lib.spec_row_softmax_stats.argtypes = [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.spec_row_softmax_stats.restype = ctypes.c_int
+_lib.spec_sample_rows_workspace_bytes.argtypes = [_I32, _I32, _I32]
+_lib.spec_sample_rows_workspace_bytes.restype = _SZ
+_lib.spec_sample_rows.argtypes = [_P, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]
+_lib.spec_sample_rows.restype = ctypes.c_int
 _lib.spec_verify_strerror.argtypes = [ctypes.c_int]
 _lib.spec_verify_strerror.restype = ctypes.c_char_p
 _lib.spec_verify_version.restype = ctypes.c_int
@@ -142,6 +146,15 @@ def spec_row_softmax_stats(logits, dtype, rows, V, temperature, out_max, out_log
                            workspace_bytes, stream) -> int:
     return _lib.spec_row_softmax_stats(_ptr(logits), dtype, rows, V, _ptr(temperature), _ptr(out_max),
                                        _ptr(out_logz), _ptr(out_argmax), _ptr(workspace), workspace_bytes, stream)
+
+
+def spec_sample_rows_workspace_bytes(rows, V, dtype) -> int:
+    return _lib.spec_sample_rows_workspace_bytes(rows, V, dtype)
+
+
+def spec_sample_rows(logits, dtype, rows, V, temperature, u, out_tokens, workspace, workspace_bytes, stream) -> int:
+    return _lib.spec_sample_rows(_ptr(logits), dtype, rows, V, _ptr(temperature), _ptr(u), _ptr(out_tokens),
+                                 _ptr(workspace), workspace_bytes, stream)
 
 
 def spec_verify_timing_enable(enable: bool) -> int:
@@ -268,3 +281,19 @@ def row_softmax_stats(logits, temperature, *, workspace=None):
     ws = workspace if workspace is not None else _ws(dev, nbytes)
     _check(spec_row_softmax_stats(logits, dt, rows, V, temperature, mx, lz, am, ws, ws.numel(), _stream(dev)))
     return mx, lz, am
+
+
+def sample_rows(logits, temperature, u, *, workspace=None):
+    """One token per row of logits [rows, V] from softmax(l/T) with the caller's uniforms (T == 0: argmax)."""
+    V = logits.shape[-1]
+    rows = logits.numel() // V if V else 0
+    dt = logits_dtype(logits)
+    _need(logits, None, "logits")
+    _need(temperature, torch.float32, "temperature")
+    _need(u, torch.float32, "u")
+    dev = logits.device
+    out = torch.empty(rows, dtype=torch.int32, device=dev)
+    nbytes = spec_sample_rows_workspace_bytes(rows, V, dt)
+    ws = workspace if workspace is not None else _ws(dev, nbytes)
+    _check(spec_sample_rows(logits, dt, rows, V, temperature, u, out, ws, ws.numel(), _stream(dev)))
+    return out
