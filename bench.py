@@ -45,7 +45,24 @@ WORKLOAD_TEXT = {
     "mid": "mid chain verify: B=64, gamma=5, V=32000, fp32, 20 spikes +8, T=0.8",
     "tree": "token-tree verify: B=32, 64 nodes, V=152064, bf16",
     "ragged": "ragged mixed verify: B=1024, gamma_b in 1..8, V=151936, bf16, 256 greedy",
+    "sample": "draft-token sampling: one token per row of the large workload's 1280 draft rows "
+              "(V=128256, bf16, Student-t), T=1.0",
 }
+SAMPLE_METRIC = "sampled draft tokens/s + logits HBM GB/s (% of peak), 1280 rows V=128256"
+
+
+def make_inputs(name):
+    """Seeded synthetic inputs of a workload (numpy)."""
+    import numpy as np
+
+    import inputgen
+    if name == "sample":
+        d = inputgen.make("large")
+        rows = np.ascontiguousarray(d["draft"].reshape(-1, d["draft"].shape[-1]))
+        n = rows.shape[0]
+        return {"logits": rows, "temperature": np.ones(n, np.float32),
+                "u": inputgen.uniform24(41, inputgen.S_USAMP, n)}
+    return inputgen.make(name)
 
 
 def device_inputs(d, dev):
@@ -82,6 +99,11 @@ def host_cores() -> int:
 def workload_accounting(name, d):
     """(positions, formula bytes, row-statistics algorithmic bytes) per step."""
     import numpy as np
+    if name == "sample":
+        rows, V = d["logits"].shape
+        es = 4 if d["logits"].dtype == np.float32 else 2
+        # one read of every row, and one extra pass over each row for the draw
+        return rows, 2 * rows * V * es, rows * V * es
     es = 4 if d["target"].dtype == np.float32 else 2
     V = d["target"].shape[-1]
     T = d["temperature"]
@@ -106,6 +128,8 @@ def workload_accounting(name, d):
 
 def make_call(sv, name, t, d):
     """Closure running one verify step on device tensors t."""
+    if name == "sample":
+        return lambda tt: sv.sample_rows(tt["logits"], tt["temperature"], tt["u"])
     if name == "tree":
         return lambda tt: sv.verify_tree(tt["target"], tt["draft"], tt["node_tokens"], tt["parents"],
                                          tt["u_accept"], tt["u_sample"], tt["temperature"], d["max_depth"])
@@ -119,6 +143,8 @@ def make_call(sv, name, t, d):
 
 def oracle_call(name, d, nthreads):
     import oracle
+    if name == "sample":
+        return oracle.sample_rows(d["logits"], d["temperature"], d["u"], nthreads=nthreads)
     if name == "tree":
         return oracle.verify_tree(d["target"], d["draft"], d["node_tokens"], d["parents"], d["u_accept"],
                                   d["u_sample"], d["temperature"], d["max_depth"], nthreads=nthreads)
@@ -129,13 +155,14 @@ def oracle_call(name, d, nthreads):
                                d["temperature"], nthreads=nthreads)
 
 
-def load_traffic(algo_bytes):
-    """HBM bytes per launch from committed PMC counters, if they match the current kernel source."""
+def load_traffic(name):
+    """HBM bytes per launch from committed PMC counters, if they were taken on this workload and
+    match the current kernel source."""
     if not os.path.exists(PMC_FILE):
         return None
     with open(PMC_FILE) as f:
         pmc = json.load(f)
-    if pmc.get("kernel_source_hash") != kernel_source_hash():
+    if pmc.get("kernel_source_hash") != kernel_source_hash() or pmc.get("workload") != WORKLOAD_TEXT[name]:
         return None
     return pmc.get("hbm_bytes_per_launch")
 
@@ -149,7 +176,7 @@ def run_bench(args):
 
     name = args.workload
     t0 = time.time()
-    d = inputgen.make(name)
+    d = make_inputs(name)
     print(f"bench: generated {name} inputs in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
     copies = [device_inputs(d, dev) for _ in range(args.copies)]
@@ -198,15 +225,23 @@ def run_bench(args):
             cpu_steps += 1
             cpu_s = time.perf_counter() - tc
         print(f"bench: oracle {cpu_steps} steps in {cpu_s:.2f} s on {cores} threads", file=sys.stderr, flush=True)
-    na = outs[-1].cpu().numpy()
-    out_tok = outs[0].cpu().numpy()
-    parity_ok = None if ref is None else bool(np.array_equal(na, ref["num_accepted"]) and
-                                              np.array_equal(out_tok, ref["out_tokens"]))
+    sample = name == "sample"
+    if sample:
+        tok = outs.cpu().numpy()
+        parity_ok = None if ref is None else bool(np.array_equal(tok, ref["tokens"]))
+    else:
+        na = outs[-1].cpu().numpy()
+        out_tok = outs[0].cpu().numpy()
+        parity_ok = None if ref is None else bool(np.array_equal(na, ref["num_accepted"]) and
+                                                  np.array_equal(out_tok, ref["out_tokens"]))
+    unit = "sampled draft tokens/s" if sample else "verified draft positions/s"
+    what = "sampling calls" if sample else "full verify steps"
+    per = "rows" if sample else "positions"
 
     line = {
-        "metric": METRIC,
+        "metric": SAMPLE_METRIC if sample else METRIC,
         "value": round(value, 1),
-        "unit": "verified draft positions/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -215,10 +250,10 @@ def run_bench(args):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "input_dtype": "bf16" if d["target"].dtype == np.uint16 else "f32",
+        "input_dtype": "bf16" if d["logits" if sample else "target"].dtype == np.uint16 else "f32",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[name], "B": int(d["temperature"].shape[0]),
-                   "V": int(d["target"].shape[-1]), "positions_per_step": positions,
+                   "V": int(d["logits" if sample else "target"].shape[-1]), "positions_per_step": positions,
                    "input_copies_rotated": args.copies},
         "logits_gbps_formula": round(gbps, 1),
         "hbm_peak_frac_formula": round(gbps / HBM_PEAK_GBPS, 4),
@@ -230,7 +265,7 @@ def run_bench(args):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(k1_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": load_traffic(k1_bytes),
+            "traffic": load_traffic(name),
             "algorithmic_bytes_per_launch": k1_bytes,
             "avg_launch_ms": round(k1_avg_ms, 5),
             "launches_timed": len(k1_ms),
@@ -238,15 +273,16 @@ def run_bench(args):
         },
         "cpu_baseline": None if ref is None else {
             "value": round(positions * cpu_steps / cpu_s, 1),
-            "unit": "verified draft positions/s",
+            "unit": unit,
             "cores": cores,
             "kind": "oracle",
-            "sample": f"{cpu_steps} full verify steps of the same batch ({positions} positions each), "
+            "sample": f"{cpu_steps} {what} of the same batch ({positions} {per} each), "
                       f"fp64 oracle, {cores} threads, {cpu_s:.2f} s wall",
         },
-        "mean_num_accepted": round(float(np.mean(na[na >= 0])), 4),
         "parity_vs_oracle": parity_ok,
     }
+    if not sample:
+        line["mean_num_accepted"] = round(float(np.mean(na[na >= 0])), 4)
     print(json.dumps(line), flush=True)
     return 0 if parity_ok is not False else 1
 

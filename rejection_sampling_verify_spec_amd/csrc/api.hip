@@ -224,13 +224,14 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int32_
   SampleJob* jobs = reinterpret_cast<SampleJob*>(ws + cv.jobs);
   TileRec* recs = reinterpret_cast<TileRec*>(ws + cv.recs);
   Layout L{LAYOUT_TREE, B, N, nullptr, 0, RT, RD};
-  if ((rc = launch_stats(dtype, target_logits, draft_logits, V, L, temperature, part, st))) return rc;
+  int* done = reinterpret_cast<int*>(ws + cv.done);
+  if ((rc = launch_stats(dtype, target_logits, draft_logits, V, L, temperature, part, st, done))) return rc;
   if (launch_accept_tree(dtype, target_logits, draft_logits, V, L, max_depth, node_tokens, parents, u_accept,
                          u_sample, temperature, part, nchunk_for(V, dtype), out_tokens, out_nodes, num_accepted,
                          jobs, st) != hipSuccess)
     return SV_EHIP;
-  if (launch_finish_jobs(dtype, target_logits, draft_logits, V, B, jobs, recs, out_tokens, max_depth + 1,
-                         force_exact_residual(), st) != hipSuccess)
+  if (launch_finish_jobs(dtype, target_logits, draft_logits, V, B, jobs, recs, part, nchunk_for(V, dtype), RT, done,
+                         out_tokens, max_depth + 1, force_exact_residual(), st) != hipSuccess)
     return SV_EHIP;
   return SV_OK;
 }
@@ -270,12 +271,14 @@ int spec_sample_rows(const void* logits, int32_t dtype, int32_t rows, int32_t V,
   Partial* part = reinterpret_cast<Partial*>(ws + cv.part);
   SampleJob* jobs = reinterpret_cast<SampleJob*>(ws + cv.jobs);
   TileRec* recs = reinterpret_cast<TileRec*>(ws + cv.recs);
+  int* done = reinterpret_cast<int*>(ws + cv.done);
   Layout L{LAYOUT_ROWS, rows, 0, nullptr, 0, rows, 0};
-  if ((rc = launch_stats(dtype, logits, nullptr, V, L, temperature, part, st))) return rc;
-  if (launch_sample_jobs(part, nchunk_for(V, dtype), rows, temperature, u, jobs, out_tokens, st) != hipSuccess)
+  if ((rc = launch_stats(dtype, logits, nullptr, V, L, temperature, part, st, done))) return rc;
+  if (launch_sample_jobs(dtype, logits, V, part, nchunk_for(V, dtype), chunk_vecs(), rows, temperature, u, jobs,
+                         out_tokens, st) != hipSuccess)
     return SV_EHIP;
-  if (launch_finish_jobs(dtype, logits, logits, V, rows, jobs, recs, out_tokens, 1, force_exact_residual(), st) !=
-      hipSuccess)
+  if (launch_finish_jobs(dtype, logits, logits, V, rows, jobs, recs, part, nchunk_for(V, dtype), rows, done,
+                         out_tokens, 1, force_exact_residual(), st) != hipSuccess)
     return SV_EHIP;
   return SV_OK;
 }

@@ -1,8 +1,8 @@
-// finish.hip -- the draw of token-tree requests as kernels of their own, after
-// the tree acceptance kernel has written one sampling job per request:
-//   k_tiles (G workgroups per request): the tile pass over the drawn row(s);
-//   k_pick (one workgroup per request): the inverse-CDF search over the tile
-//   records.
+// finish.hip -- the draw as a kernel of its own, after a kernel has written
+// one sampling job per request (token trees) or per row (draft sampling):
+// k_draw_jobs, G workgroups per job, runs the tile pass over the drawn row(s)
+// and, in the last workgroup to finish, the inverse-CDF pick over the tile
+// records.
 // The draw itself (tail.h) is the one the chain kernel runs [Primer 考点2
 // residual; 考点4 bonus].
 #include "tail.h"
@@ -11,84 +11,121 @@ namespace sv {
 
 constexpr int kNW = 4;  // waves per workgroup
 
-// Workgroup (b, g), g < G: tiles g*kNW + i*G*kNW + [0, kNW) of request b's
-// drawn row(s), one per wave.
-template <int DT>
-__global__ __launch_bounds__(kNW * 64) void k_tiles(const void* __restrict__ tgt, const void* __restrict__ dft, int V,
-                                               int G, const SampleJob* __restrict__ jobs,
-                                               TileRec* __restrict__ recs) {
-  __shared__ TileSpace<kNW> ts;
-  __shared__ double exp2tab[64];
-  __shared__ SampleJob sj;
-  const int b = blockIdx.x / G, g = blockIdx.x - b * G;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (threadIdx.x < 64) exp2tab[threadIdx.x] = exp2_f64((double)threadIdx.x * 0.015625);
-  if (threadIdx.x == 0) sj = jobs[b];
-  __syncthreads();
-  const SampleJob J = uniform_job(sj);
-  if (J.kind == JOB_NONE) return;
-  constexpr int es = sizeof(typename Elem<DT>::T);
-  const char* trow = reinterpret_cast<const char*>(tgt) + (size_t)J.trow * (size_t)V * es;
-  const char* drow = reinterpret_cast<const char*>(dft) + (size_t)J.drow * (size_t)V * es;
-  const int ntile = tiles_per_row(V, DT);
-  TileRec* R = recs + (long long)b * ntile;
-  for (int base = g * kNW; base < ntile; base += G * kNW)
-    wave_tile<DT, kNW>(trow, drow, V, ntile, base + wv, J, R, ts, exp2tab, wv, lane);
+// A job written by an earlier kernel, read by the whole wave into scalar
+// registers (lane i loads 64-bit word i).
+__device__ __forceinline__ SampleJob load_job(const SampleJob* src, int lane) {
+  static_assert(sizeof(SampleJob) % 8 == 0, "job of 64-bit words");
+  constexpr int nw = (int)(sizeof(SampleJob) / 8);
+  uint64_t mine = 0;
+  if (lane < nw) mine = reinterpret_cast<const uint64_t*>(src)[lane];
+  uint64_t w[nw];
+#pragma unroll
+  for (int i = 0; i < nw; ++i) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mine, i);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), i);
+    w[i] = ((uint64_t)hi << 32) | lo;
+  }
+  SampleJob J;
+  __builtin_memcpy(&J, w, sizeof(J));
+  return J;
 }
 
+struct DrawArgs {
+  const void* tgt;
+  const void* dft;
+  int V;
+  int G;                 // workgroups per job
+  const SampleJob* jobs; // [B]
+  TileRec* recs;         // [B, ntile]
+  const Partial* part;   // chunk partials (masses of skipped chunks)
+  int nchunk;
+  long long RT;          // target rows: draft row d has partials at row RT + d
+  int* done;             // [B] workgroups finished with their tiles (zeroed by the streaming kernel)
+  int32_t* out;
+  int out_width;
+  int force_exact;
+};
+
+// Workgroups (b, g), g < G, of job b: wave w of workgroup g takes the tiles
+// g*kNW + w, + G*kNW, ... that are read (tiles of skipped chunks get their
+// record from the chunk's partial); the last workgroup to finish runs the pick.
 template <int DT, bool STAGED>
-__global__ __launch_bounds__(kNW * 64) void k_pick(const void* __restrict__ tgt, const void* __restrict__ dft, int V,
-                                              const SampleJob* __restrict__ jobs, TileRec* __restrict__ recs,
-                                              int32_t* __restrict__ out, int out_width, int force_exact) {
-  __shared__ PickSpace<kNW> ps;
-  __shared__ double exp2tab[64];
-  __shared__ SampleJob sj;
-  if (threadIdx.x < 64) exp2tab[threadIdx.x] = exp2_f64((double)threadIdx.x * 0.015625);
-  if (threadIdx.x == 0) sj = jobs[blockIdx.x];
-  __syncthreads();
-  const SampleJob J = uniform_job(sj);
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_draw_jobs(DrawArgs A) {
+  __shared__ union {
+    TileSpace<kNW> ts;
+    PickSpace<kNW> pick;
+  } u;
+  __shared__ double tab[64];                 // 2^{j/64}
+  __shared__ double mass_t[64], mass_d[64];  // masses of the skipped chunks
+  __shared__ int s_last;
+  const int b = blockIdx.x / A.G, g = blockIdx.x - b * A.G;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  if (tid < 64) tab[tid] = exp2_f64((double)tid * 0.015625);
+  const SampleJob J = load_job(A.jobs + b, lane);
   if (J.kind == JOB_NONE) return;
-  const int b = blockIdx.x;
+  const bool res = J.kind == JOB_RESIDUAL;
+  if (J.skip && tid < 64 && tid < A.nchunk) {
+    auto mass = [&](long long prow, float m_row) -> double {
+      const Partial q = read_partial(A.part + prow * A.nchunk + tid);
+      return q.m == -INFINITY ? 0.0
+                              : (double)partial_s(q) * exp2_f64(((double)q.m - (double)m_row) * (double)J.c32);
+    };
+    mass_t[tid] = mass(J.trow, J.mt);
+    if (res) mass_d[tid] = mass(A.RT + J.drow, J.md);
+  }
+  __syncthreads();
   constexpr int es = sizeof(typename Elem<DT>::T);
-  const char* trow = reinterpret_cast<const char*>(tgt) + (size_t)J.trow * (size_t)V * es;
-  const char* drow = reinterpret_cast<const char*>(dft) + (size_t)J.drow * (size_t)V * es;
-  const int ntile = tiles_per_row(V, DT);
-  pick<DT, kNW, STAGED>(trow, drow, V, ntile, J, recs + (long long)b * ntile,
-                        out + (long long)b * out_width + J.pos, force_exact, ps, exp2tab);
+  const char* trow = reinterpret_cast<const char*>(A.tgt) + (size_t)J.trow * (size_t)A.V * es;
+  const char* drow = reinterpret_cast<const char*>(A.dft) + (size_t)J.drow * (size_t)A.V * es;
+  const int ntile = tiles_per_row(A.V, DT);
+  TileRec* recs = A.recs + (long long)b * ntile;
+  if (res)
+    wave_tiles<DT, true, kNW>(trow, drow, A.V, ntile, g * kNW + wv, A.G * kNW, J, recs, mass_t, mass_d, u.ts, tab,
+                              wv, lane);
+  else
+    wave_tiles<DT, false, kNW>(trow, drow, A.V, ntile, g * kNW + wv, A.G * kNW, J, recs, mass_t, mass_d, u.ts, tab,
+                               wv, lane);
+  // the records are complete before the count; the last workgroup picks
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(A.done + b, 1) == A.G - 1;
+  __syncthreads();
+  if (!s_last) return;
+  pick<DT, kNW, STAGED>(trow, drow, A.V, ntile, J, recs, A.out + (long long)b * A.out_width + J.pos, A.force_exact,
+                        u.pick, tab);
 }
 
-// Workgroups per request of k_tiles: one per kNW tiles, capped so that the
-// grid stays within 2^20 workgroups.
-static int tiles_groups(int B, int V, int dt) {
-  const int ntile = tiles_per_row(V, dt);
-  int G = (ntile + kNW - 1) / kNW;
-  const long long cap = (1ll << 20) / (B > 0 ? B : 1);
-  if (G > cap) G = (int)cap;
-  return G < 1 ? 1 : G;
+namespace {
+int device_cus_finish() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0, c = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
+      c = 1;
+    cus = c;
+  }
+  return cus;
 }
+}  // namespace
 
 hipError_t launch_finish_jobs(int dt, const void* tgt, const void* dft, int V, int B, SampleJob* jobs,
-                              TileRec* recs, int32_t* out, int out_width, int force_exact, hipStream_t st) {
+                              TileRec* recs, const Partial* part, int nchunk, long long RT, int* done, int32_t* out,
+                              int out_width, int force_exact, hipStream_t st) {
   if (B == 0) return hipSuccess;
-  const int G = tiles_groups(B, V, dt);
+  // workgroups per job: enough for about four per CU, at most 8
+  const long long want = (4ll * device_cus_finish() + B - 1) / B;
+  int G = (int)(want < 1 ? 1 : (want > 8 ? 8 : want));
+  if ((long long)B * G > 0x7fffffffLL) G = 1;
+  const DrawArgs A{tgt, dft, V, G, jobs, recs, part, nchunk, RT, done, out, out_width, force_exact};
+  const dim3 grid((unsigned)((long long)B * G)), blk(kNW * 64);
   const bool staged = tiles_per_row(V, dt) <= kPickStage;
-  const dim3 blk(kNW * 64);
   if (dt == 1) {
-    hipLaunchKernelGGL(k_tiles<1>, dim3((unsigned)(B * G)), blk, 0, st, tgt, dft, V, G, jobs, recs);
-    if (staged)
-      hipLaunchKernelGGL((k_pick<1, true>), dim3((unsigned)B), blk, 0, st, tgt, dft, V, jobs, recs, out, out_width,
-                         force_exact);
-    else
-      hipLaunchKernelGGL((k_pick<1, false>), dim3((unsigned)B), blk, 0, st, tgt, dft, V, jobs, recs, out, out_width,
-                         force_exact);
+    if (staged) hipLaunchKernelGGL((k_draw_jobs<1, true>), grid, blk, 0, st, A);
+    else hipLaunchKernelGGL((k_draw_jobs<1, false>), grid, blk, 0, st, A);
   } else {
-    hipLaunchKernelGGL(k_tiles<0>, dim3((unsigned)(B * G)), blk, 0, st, tgt, dft, V, G, jobs, recs);
-    if (staged)
-      hipLaunchKernelGGL((k_pick<0, true>), dim3((unsigned)B), blk, 0, st, tgt, dft, V, jobs, recs, out, out_width,
-                         force_exact);
-    else
-      hipLaunchKernelGGL((k_pick<0, false>), dim3((unsigned)B), blk, 0, st, tgt, dft, V, jobs, recs, out, out_width,
-                         force_exact);
+    if (staged) hipLaunchKernelGGL((k_draw_jobs<0, true>), grid, blk, 0, st, A);
+    else hipLaunchKernelGGL((k_draw_jobs<0, false>), grid, blk, 0, st, A);
   }
   return hipGetLastError();
 }

@@ -5,16 +5,20 @@
 //
 // A call runs the streaming statistics kernel over the rows, then
 // k_sample_jobs (one wave per row: the row maximum from the chunk partials,
-// the greedy token for T == 0, or a bonus-type sampling job), then the tile
-// pass and pick of the verify draw over each row (finish.hip).
+// the greedy token for T == 0, or a bonus-type sampling job with the row
+// chunks it need not read), then the tile pass and pick of the verify draw
+// over each row (finish.hip).
 #include "sv_internal.h"
 
 namespace sv {
 
 constexpr int kJobRowsPerBlock = 4;  // one wave per row
 
-__global__ __launch_bounds__(kJobRowsPerBlock * 64) void k_sample_jobs(const Partial* __restrict__ part, int nchunk,
-                                                                      int rows, const float* __restrict__ temperature,
+template <int DT>
+__global__ __launch_bounds__(kJobRowsPerBlock * 64) void k_sample_jobs(const void* __restrict__ logits, int V,
+                                                                      const Partial* __restrict__ part, int nchunk,
+                                                                      int chunk_vecs, int rows,
+                                                                      const float* __restrict__ temperature,
                                                                       const float* __restrict__ u,
                                                                       SampleJob* __restrict__ jobs,
                                                                       int32_t* __restrict__ out) {
@@ -50,8 +54,26 @@ __global__ __launch_bounds__(kJobRowsPerBlock * 64) void k_sample_jobs(const Par
       idx = i2;
     }
   }
-  if (lane != 0) return;
   const bool ok = t_ok && !bad && M > -INFINITY && M < INFINITY;
+  // Row chunks whose maximum lies more than -kTinyExp below the row maximum
+  // hold only masses below 2^-50 of it (at most 2^-36 in all): their tiles are
+  // not read again, their mass comes from the partial (16-byte aligned rows,
+  // so that chunks start on tile boundaries).
+  constexpr int es = sizeof(typename Elem<DT>::T), epv = Elem<DT>::kPerVec;
+  const long long ctok = (long long)chunk_vecs * epv;
+  const int tok = tile_tokens(DT);
+  const bool row_aligned =
+      ((reinterpret_cast<uintptr_t>(logits) + (uintptr_t)r * (uintptr_t)V * es) & 15u) == 0;
+  unsigned long long skip = 0ull;
+  if (ok && !greedy && row_aligned && nchunk > 1 && nchunk <= 64 && ctok % tok == 0) {
+    bool tiny = false;
+    if (lane < nchunk) {
+      const Partial q = read_partial(part + r * nchunk + lane);
+      tiny = q.m == -INFINITY || (q.m - M) * c32_of(T) < kTinyExp;
+    }
+    skip = __ballot(tiny);
+  }
+  if (lane != 0) return;
   SampleJob J{};
   J.kind = JOB_NONE;
   if (ok && greedy) {
@@ -67,8 +89,8 @@ __global__ __launch_bounds__(kJobRowsPerBlock * 64) void k_sample_jobs(const Par
     J.mt = M;
     J.md = 0.0f;
     J.u = ur;
-    J.skip = 0ull;
-    J.chunk_tiles = 0;
+    J.skip = skip;
+    J.chunk_tiles = skip ? (int)(ctok / tok) : 0;
     J.slow = 0.0;
   } else {
     out[r] = -1;
@@ -76,12 +98,18 @@ __global__ __launch_bounds__(kJobRowsPerBlock * 64) void k_sample_jobs(const Par
   jobs[r] = J;
 }
 
-hipError_t launch_sample_jobs(const Partial* part, int nchunk, int rows, const float* temperature, const float* u,
-                              SampleJob* jobs, int32_t* out, hipStream_t st) {
+hipError_t launch_sample_jobs(int dt, const void* logits, int V, const Partial* part, int nchunk, int chunk_vecs,
+                              int rows, const float* temperature, const float* u, SampleJob* jobs, int32_t* out,
+                              hipStream_t st) {
   if (rows == 0) return hipSuccess;
   const long long grid = ((long long)rows + kJobRowsPerBlock - 1) / kJobRowsPerBlock;
-  hipLaunchKernelGGL(k_sample_jobs, dim3((unsigned)grid), dim3(kJobRowsPerBlock * 64), 0, st, part, nchunk, rows,
-                     temperature, u, jobs, out);
+  const dim3 g((unsigned)grid), b(kJobRowsPerBlock * 64);
+  if (dt == 1)
+    hipLaunchKernelGGL(k_sample_jobs<1>, g, b, 0, st, logits, V, part, nchunk, chunk_vecs, rows, temperature, u,
+                       jobs, out);
+  else
+    hipLaunchKernelGGL(k_sample_jobs<0>, g, b, 0, st, logits, V, part, nchunk, chunk_vecs, rows, temperature, u,
+                       jobs, out);
   return hipGetLastError();
 }
 

@@ -244,9 +244,11 @@ hipError_t launch_verify_chain(int dt, const void* tgt, const void* dft, int V, 
                                int32_t* out, int out_width, int32_t* num_acc, float* diag, int force_exact,
                                hipStream_t st);
 hipError_t launch_finish_jobs(int dt, const void* tgt, const void* dft, int V, int B, SampleJob* jobs,
-                              TileRec* recs, int32_t* out, int out_width, int force_exact, hipStream_t st);
-hipError_t launch_sample_jobs(const Partial* part, int nchunk, int rows, const float* temperature, const float* u,
-                              SampleJob* jobs, int32_t* out, hipStream_t st);
+                              TileRec* recs, const Partial* part, int nchunk, long long RT, int* done, int32_t* out,
+                              int out_width, int force_exact, hipStream_t st);
+hipError_t launch_sample_jobs(int dt, const void* logits, int V, const Partial* part, int nchunk, int chunk_vecs,
+                              int rows, const float* temperature, const float* u, SampleJob* jobs, int32_t* out,
+                              hipStream_t st);
 hipError_t launch_stats_finalize(const Partial* part, int nchunk, int rows, const float* temperature,
                                  float* out_max, float* out_logz, int32_t* out_argmax, hipStream_t st);
 

@@ -921,24 +921,6 @@ __device__ __forceinline__ void tile_pass(uint4 (&wt)[4], uint4 (&wd)[4], const 
   write_rec(rec, zt, zd, dp, bp, ng, gt, gd, lane);
 }
 
-// One wave's tile k (if below ntile); tiles of skipped chunks are the caller's.
-template <int DT, int NW>
-__device__ __forceinline__ void wave_tile(const char* trow, const char* drow, int V, int ntile, int k,
-                                          const SampleJob& J, TileRec* R, TileSpace<NW>& TS, const double* tab, int wv,
-                                          int lane) {
-  constexpr int tok = TileTok<DT>::value;
-  if (k >= ntile) return;
-  const bool res = J.kind == JOB_RESIDUAL;
-  uint4 wt[4], wd[4];
-  load_tile_wave<DT>(trow, k * tok, V, lane, wt);
-  auto none = [] {};
-  if (res) {
-    load_tile_wave<DT>(drow, k * tok, V, lane, wd);
-    tile_pass<DT, true, NW>(wt, wd, J, R + k, TS, tab, wv, lane, none);
-  } else {
-    tile_pass<DT, false, NW>(wt, wt, J, R + k, TS, tab, wv, lane, none);
-  }
-}
 
 // One wave's tiles k0, k0 + step, ... below ntile: a tile of a skipped chunk
 // gets its record from the chunk's mass; the others take the tile pass.
