@@ -239,7 +239,8 @@ def run_bench(args):
     per = "rows" if sample else "positions"
 
     line = {
-        "metric": SAMPLE_METRIC if sample else METRIC,
+        "metric": SAMPLE_METRIC if sample else (METRIC if name == "large" else
+                                                f"verified draft positions/s + logits HBM GB/s (% of peak), {name}"),
         "value": round(value, 1),
         "unit": unit,
         "n_gpus": 1,
