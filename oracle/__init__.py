@@ -180,3 +180,9 @@ def sample_rows(logits, temperature, u, nthreads=None):
     if rc != 0:
         raise RuntimeError("oracle_sample_rows failed")
     return dict(tokens=out, margin=margin)
+
+
+# KV-cache steps around verification (plain Python/numpy, no C)
+from .cache import (  # noqa: E402,F401
+    draft_window, kv_commit, kv_valid_slots, max_window_blocks, slot, valid_slots, window_one,
+)
