@@ -47,7 +47,13 @@ WORKLOAD_TEXT = {
     "ragged": "ragged mixed verify: B=1024, gamma_b in 1..8, V=151936, bf16, 256 greedy",
     "sample": "draft-token sampling: one token per row of the large workload's 1280 draft rows "
               "(V=128256, bf16, Student-t), T=1.0",
+    "kv": "KV commit into sink + ring caches after a B=256, gamma=5 verify step: 256 rows (32 layers x 8 KV "
+          "heads) x 256 B (head dim 128, bf16) per position, S=4 sinks + W=1020 ring slots, lengths ~ U[0, 4096), "
+          "accepted drafts from 5 Bernoulli(0.8) trials",
+    "window": "draft-KV window: B=256, W=2048, block 128, future offset 5, lengths ~ U{0..40960}, "
+              "full block table 256 x 320",
 }
+CACHE_WORKLOADS = ("kv", "window")
 SAMPLE_METRIC = "sampled draft tokens/s + logits HBM GB/s (% of peak), 1280 rows V=128256"
 
 
@@ -165,6 +171,173 @@ def load_traffic(name):
     if pmc.get("kernel_source_hash") != kernel_source_hash() or pmc.get("workload") != WORKLOAD_TEXT[name]:
         return None
     return pmc.get("hbm_bytes_per_launch")
+
+
+def _timed_loop(args, sv, call, copies):
+    """Warmup, then args.steps timed calls with the library's kernel events on every
+    args.time_every-th call. Returns (elapsed s, kernel ms list, last output)."""
+    import torch
+    for i in range(args.warmup):
+        call(copies[i % len(copies)])
+    torch.cuda.synchronize()
+    sv.spec_verify_timing_reset()
+    torch.cuda.synchronize()
+    start = time.perf_counter()
+    outs = None
+    for i in range(args.steps):
+        timed = i % args.time_every == 0
+        if timed:
+            sv.spec_verify_timing_enable(True)
+        outs = call(copies[i % len(copies)])
+        if timed:
+            sv.spec_verify_timing_enable(False)
+    torch.cuda.synchronize()
+    return time.perf_counter() - start, sv.spec_verify_timing_read(args.steps), outs
+
+
+def kv_copied_positions(d):
+    """Positions a commit copies: the kept positions P..P+n, less those whose ring slot a later kept
+    position takes."""
+    S, W = d["sink"], d["window"]
+    total = 0
+    for P, n in zip(d["lengths"].tolist(), d["num_accepted"].tolist()):
+        total += sum(1 for p in range(P, P + n + 1) if p < S or p + W > P + n)
+    return total
+
+
+def run_cache_bench(args):
+    """The KV-cache steps: the commit into sink + ring caches (kv) and the draft-KV window (window)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import rejection_sampling_verify_spec_amd as sv
+
+    name = args.workload
+    d = make_inputs(name)
+    dev = torch.device("cuda:0")
+    cores = 1  # the oracle of these steps is single-threaded numpy
+    if name == "kv":
+        B = d["lengths"].shape[0]
+        S, W, R, E, gamma = d["sink"], d["window"], d["rows"], d["row_bytes"], d["gamma"]
+        cap = S + W
+        kc = torch.empty((B, R, cap, E), dtype=torch.uint8, device=dev)
+        vc = torch.empty_like(kc)
+        copies = [device_inputs({"k_new": d["k_new"], "v_new": d["v_new"]}, dev) for _ in range(args.copies)]
+        lens_t = torch.from_numpy(d["lengths"]).to(dev)
+        n_t = torch.from_numpy(d["num_accepted"]).to(dev)
+
+        def call(t):
+            return sv.kv_commit(kc, vc, t["k_new"], t["v_new"], lens_t, n_t, S, W)
+        units = int((d["num_accepted"] + 1).sum())
+        algo = kv_copied_positions(d) * R * E * 2 * 2  # K and V rows, read once and written once
+        kernel, unit, dtype = "k_kv_commit", "committed KV positions/s", "u8"
+        metric = "committed KV positions/s + KV HBM GB/s (% of peak), B=256 gamma=5, 256 rows x 256 B"
+    else:
+        B, cols = d["block_table"].shape
+        W, bs, K = d["window"], d["block_size"], d["future_offset"]
+        wc = sv.spec_draft_window_max_blocks(W, bs)
+        copies = [device_inputs({"seq_lens": d["seq_lens"], "block_table": d["block_table"]}, dev)
+                  for _ in range(args.copies)]
+
+        def call(t):
+            return sv.draft_window(t["seq_lens"], t["block_table"], W, bs, K, window_cols=wc)
+        units = B
+        ref_all = oracle.draft_window(d["seq_lens"], W, bs, K, d["block_table"], wc)
+        gathered = int((ref_all["block_table"] != 0).sum())
+        algo = 4 * (B + gathered + B * wc + B)  # lengths read, block ids gathered, table and lengths written
+        kernel, unit, dtype = "k_draft_window", "windowed requests/s", "int32"
+        metric = "windowed requests/s + table HBM GB/s, B=256 W=2048 block 128"
+
+    elapsed, k_ms, outs = _timed_loop(args, sv, call, copies)
+    print(f"bench: {args.steps} steps in {elapsed * 1e3:.2f} ms", file=sys.stderr, flush=True)
+    k_avg_ms = float(np.mean(k_ms)) if k_ms else float("nan")
+    k_gbps = algo / (k_avg_ms * 1e-3) / 1e9
+
+    ref = None
+    cpu_calls, cpu_s, cpu_units = 0, 0.0, 0
+    parity_ok = None
+    if name == "kv":
+        # the oracle on a sample of 8 requests, from the caches the GPU left after the warmup and timed
+        # steps (every step commits the same batch, so a further commit changes nothing)
+        ns = 8
+        kc_h = kc[:ns].cpu().numpy()
+        vc_h = vc[:ns].cpu().numpy()
+        zc = np.zeros((B, 1, cap, 0), np.uint8)
+        zn = np.zeros((B, gamma + 1, 1, 0), np.uint8)
+        ref_len = oracle.kv_commit(zc, zc.copy(), zn, zn.copy(), d["lengths"], d["num_accepted"], S, W)
+        lens_ok = bool(np.array_equal(outs.cpu().numpy(), ref_len))
+        sample_units = int((d["num_accepted"][:ns] + 1).sum())
+        if not args.skip_cpu_baseline:
+            # start the oracle from other contents, so that its writes are the ones compared
+            kc_o = np.zeros_like(kc_h)
+            vc_o = np.zeros_like(vc_h)
+            tc = time.perf_counter()
+            while cpu_calls == 0 or cpu_s < args.cpu_seconds:
+                oracle.kv_commit(kc_o, vc_o, d["k_new"][:ns], d["v_new"][:ns], d["lengths"][:ns],
+                                 d["num_accepted"][:ns], S, W)
+                cpu_calls += 1
+                cpu_s = time.perf_counter() - tc
+            cpu_units = sample_units * cpu_calls
+            # the slots this step wrote must agree; the others hold what earlier contents left
+            rows_ok = True
+            for b in range(ns):
+                P, n = int(d["lengths"][b]), int(d["num_accepted"][b])
+                for s_ in {oracle.slot(p, S, W) for p in range(P, P + n + 1)}:
+                    rows_ok &= bool(np.array_equal(kc_o[b, :, s_], kc_h[b, :, s_]) and
+                                    np.array_equal(vc_o[b, :, s_], vc_h[b, :, s_]))
+            parity_ok = lens_ok and rows_ok
+            sample = (f"{cpu_calls} commits of 8 of the 256 requests ({sample_units} kept positions each), numpy "
+                      f"oracle, 1 thread, {cpu_s:.2f} s wall")
+    else:
+        got_l, got_t = (o.cpu().numpy() for o in outs)
+        parity_ok = bool(np.array_equal(got_l, ref_all["windowed_lens"]) and
+                         np.array_equal(got_t, ref_all["block_table"]))
+        if not args.skip_cpu_baseline:
+            tc = time.perf_counter()
+            while cpu_calls == 0 or cpu_s < args.cpu_seconds:
+                oracle.draft_window(d["seq_lens"], W, bs, K, d["block_table"], wc)
+                cpu_calls += 1
+                cpu_s = time.perf_counter() - tc
+            cpu_units = B * cpu_calls
+            sample = f"{cpu_calls} calls over all {B} requests, numpy oracle, 1 thread, {cpu_s:.2f} s wall"
+    line = {
+        "metric": metric,
+        "value": round(units * args.steps / elapsed, 1),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[name], "B": int(B), "units_per_step": units,
+                   "input_copies_rotated": args.copies},
+        "hbm_gbps_algorithmic": round(algo * args.steps / elapsed / 1e9, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": kernel,
+            "achieved": round(k_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(k_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": algo,
+            "avg_launch_ms": round(k_avg_ms, 5),
+            "launches_timed": len(k_ms),
+            "timed_every_nth_step": args.time_every,
+        },
+        "cpu_baseline": None if cpu_calls == 0 else {
+            "value": round(cpu_units / cpu_s, 1), "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": sample,
+        },
+        "parity_vs_oracle": parity_ok,
+    }
+    print(json.dumps(line), flush=True)
+    return 0 if parity_ok is not False else 1
 
 
 def run_bench(args):
@@ -416,6 +589,8 @@ def main():
         return 2
     if args.copy_calibration:
         return copy_calibration(args)
+    if args.workload in CACHE_WORKLOADS:
+        return run_cache_bench(args)
     return run_bench(args)
 
 

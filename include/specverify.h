@@ -72,6 +72,8 @@ typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 #define SV_MAX_GAMMA 256       /* drafted positions per request          */
 #define SV_MAX_TREE_NODES 1024 /* nodes per token tree (root included)    */
 #define SV_MAX_VOCAB (1 << 28)
+#define SV_MAX_KV_SLOTS (1 << 30)     /* sink + window slots of one KV cache      */
+#define SV_MAX_KV_ROW_BYTES (1 << 30) /* bytes of one cache row (one head, one position) */
 
 /* Workspace bytes needed by spec_verify for these sizes (0 on bad sizes). */
 size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t dtype);
@@ -201,6 +203,101 @@ size_t spec_sample_rows_workspace_bytes(int32_t rows, int32_t V, int32_t dtype);
 int spec_sample_rows(const void* logits, int32_t dtype, int32_t rows, int32_t V, const float* temperature,
                      const float* u, int32_t* out_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * KV commit after verification into a sink + ring cache.
+ *
+ * The cache keeps the first S positions in fixed slots and the most recent W
+ * in a ring; position pos lives in slot Slot(pos) = pos for pos < S, else
+ * S + ((pos - S) mod W) [Edge 环形上下文与注意力沉淀机制]. Per request the
+ * pool holds, for each of R rows (R = layers * kv_heads), the S+W slots of E
+ * bytes each: k_cache and v_cache are [B, R, S+W, E], as in the pool of
+ * [Edge C++ 环形 KV 缓存管理内核实现] with one pool per request.
+ *
+ * The target pass that verified gamma drafts produced keys and values for the
+ * gamma+1 positions P .. P+gamma (P = lengths[b]: the pending token, then the
+ * drafts) [Primer 考点1]; the caller stages them in k_new and v_new,
+ * [B, gamma+1, R, E]. Verification kept n = num_accepted[b] drafts, so the
+ * request keeps n+1 positions [Primer 考点4]: positions P .. P+n are copied to
+ * their slots (a later one wins when two share a slot, W < n+1) and
+ * new_lengths[b] = P + n + 1. Rejected positions are never written, so the
+ * window positions they would have displaced stay valid: the rollback costs
+ * nothing. A request with n outside [0, gamma] (for instance the -1 that
+ * verification reports for a bad request), a negative length, or a length that
+ * would pass 2^31-1 writes nothing and keeps its length.
+ *
+ *   k_cache, v_cache  device, [B, R, S+W, E] bytes, updated in place
+ *   k_new, v_new      device, [B, gamma+1, R, E] bytes, read
+ *   lengths           device int32 [B], read
+ *   num_accepted      device int32 [B] (the output of a verify call), read
+ *   new_lengths       device int32 [B], written; must not overlap lengths
+ *   rows = R >= 1, row_bytes = E in [1, SV_MAX_KV_ROW_BYTES], sink = S >= 0,
+ *   window = W >= 1, S + W <= SV_MAX_KV_SLOTS, 0 <= gamma <= SV_MAX_GAMMA
+ * The element type is the caller's: rows are copied as bytes (16-byte
+ * accesses when E and every base pointer are 16-byte multiples). The caches
+ * must not overlap each other or the staging buffers. Asynchronous on
+ * `stream`, allocates nothing. Returns SV_EINVAL (bad size, null pointer,
+ * k_cache == v_cache, overlapping length arrays) or SV_EHIP; nothing is
+ * enqueued on a host-side error.
+ */
+int spec_kv_commit(void* k_cache, void* v_cache, const void* k_new, const void* v_new, const int32_t* lengths,
+                   const int32_t* num_accepted, int32_t* new_lengths, int32_t B, int32_t gamma, int32_t rows,
+                   int64_t row_bytes, int32_t sink, int32_t window, void* stream);
+
+/*
+ * The slots a sink + ring cache of length P holds, in logical order, for an
+ * attention pass to read [Edge C++ 环形 KV 缓存管理内核实现]: while
+ * P <= S+W, slots 0 .. P-1; after that the S sink slots, then the slots of
+ * positions P-W .. P-1.
+ *   lengths    device int32 [B]
+ *   slots      device int32 [B, S+W]: the slots, -1 past the count
+ *   positions  device int32 [B, S+W] or NULL: the logical position held in
+ *              each listed slot (for position-dependent encodings), -1 past
+ *              the count
+ *   counts     device int32 [B]: min(max(P, 0), S+W)
+ * Returns SV_EINVAL or SV_EHIP; asynchronous on `stream`.
+ */
+int spec_kv_valid_slots(const int32_t* lengths, int32_t B, int32_t sink, int32_t window, int32_t* slots,
+                        int32_t* positions, int32_t* counts, void* stream);
+
+/*
+ * Draft-KV sliding window over a paged KV cache [Window 窗口数学; Window block
+ * table 的裁剪方式; Window 两条贯穿始终的不变量].
+ *
+ * The draft model reads only a window of about W tokens ending K tokens past
+ * the context length (K = future_offset: the draft query positions beyond
+ * seq_lens); the target model and every KV write keep the full table. Per
+ * request with length L: start = floor(max(L + K - W, 0) / b) * b (b =
+ * block_size), windowed length L - start (at most W - K + b - 1), start block
+ * start / b, blocks needed ceil((L - start) / b).
+ *   seq_lens       device int32 [B]
+ *   block_table    device int32 [B, full_cols], the full table (read only;
+ *                  may be NULL when full_cols == 0)
+ *   windowed_lens  device int32 [B]: L - start, -1 for a negative L; may be
+ *                  seq_lens itself (in place), must not overlap it otherwise
+ *   window_table   device int32 [B, window_cols]: row i holds
+ *                  block_table[i, start_block + j] for j < needed while
+ *                  start_block + j < full_cols, 0 elsewhere. Windowed index t
+ *                  then addresses the same KV as absolute position start + t.
+ * window_cols must be at least spec_draft_window_max_blocks(window,
+ * block_size) = ceil((W + b - 1) / b), the most blocks a window can span
+ * (W/b + 1 when b divides W). Requires W >= 1, b >= 1, 0 <= K <= W.
+ * Returns SV_EINVAL or SV_EHIP; asynchronous on `stream`.
+ */
+int32_t spec_draft_window_max_blocks(int32_t window, int32_t block_size);
+int spec_draft_window(const int32_t* seq_lens, int32_t B, int32_t window, int32_t block_size, int32_t future_offset,
+                      const int32_t* block_table, int32_t full_cols, int32_t* windowed_lens, int32_t* window_table,
+                      int32_t window_cols, void* stream);
+
+/*
+ * The same windowed length for HOST arrays (the host copies of the length
+ * inputs of an attention pass), with the arithmetic of spec_draft_window, so
+ * that every copy of a length gets one transform [Window 两条贯穿始终的不变量].
+ * Synchronous; seq_lens and windowed_lens are host int32 [n] and may be the
+ * same array.
+ */
+int spec_draft_window_host(const int32_t* seq_lens, int32_t n, int32_t window, int32_t block_size,
+                           int32_t future_offset, int32_t* windowed_lens);
+
 /* Human-readable text for an sv_status. */
 const char* spec_verify_strerror(int status);
 
@@ -209,9 +306,10 @@ int spec_verify_version(void);
 
 /*
  * Optional timing of the streaming row-statistics kernel inside the calls
- * above. While recording is on, each call records a pair of HIP events around
- * that kernel on `stream`. spec_verify_timing_enable(1) starts or resumes
- * recording, spec_verify_timing_enable(0) pauses it (recorded pairs are kept),
+ * above (in spec_kv_commit and spec_draft_window: of their one kernel). While
+ * recording is on, each call records a pair of HIP events around that kernel
+ * on `stream`. spec_verify_timing_enable(1) starts or resumes recording,
+ * spec_verify_timing_enable(0) pauses it (recorded pairs are kept),
  * spec_verify_timing_reset() forgets them. spec_verify_timing_read returns the
  * recorded per-call durations (ms), after the caller synchronised the stream;
  * at most `max` values are written and *count receives how many are available

@@ -15,6 +15,11 @@ tree       B=32, 64 nodes (root + 4 + 16 + 43, depth 3), V=152064, bf16; target 
            draft row of node v = target row of parent(v) + N(0, 0.7); T=1.0
 ragged     B=1024, gamma_b ~ U{1..8}, V=151936, bf16; target ~ N(0, sd 3); draft = target + N(0, sigma_b),
            sigma_b ~ U[0.2, 2.0]; 256 requests (seeded permutation) greedy T=0, the rest T ~ U(0.5, 1.2)
+kv         KV commit after a B=256, gamma=5 verify step: R=256 rows (32 layers x 8 KV heads) of E=256
+           bytes (head dim 128, bf16) per position; S=4 sinks + W=1020 ring slots; lengths ~ U[0, 4096);
+           accepted drafts = leading successes of 5 Bernoulli(0.8) trials; keys/values random bytes
+window     draft-KV window: B=256, W=2048, block 128, future offset K=5; lengths ~ U{0..40960};
+           full block table [256, 320] of distinct block ids
 =========  =====================================================================
 
 Draft tokens are drawn from softmax(draft row / T) of the *stored* draft row
@@ -35,6 +40,7 @@ _SRC = os.path.join(_HERE, "gen.c")
 _LIB = os.path.join(_HERE, "libinputgen.so")
 
 S_TOKENS, S_UACC, S_USAMP, S_GAMMA, S_SIGMA, S_TEMP, S_PERM, S_TREE = 4, 5, 6, 7, 8, 9, 10, 11
+S_KV, S_LEN, S_ACC, S_TABLE = 12, 13, 14, 15
 DIST_NORMAL, DIST_T3 = 0, 1
 
 _lib = None
@@ -61,6 +67,7 @@ def _load():
         lib.ig_uniform24.argtypes = [U64, U32, I64, P, I]
         lib.ig_uniform53.argtypes = [U64, U32, I64, P, I]
         lib.ig_normal.argtypes = [U64, U32, I64, P, I]
+        lib.ig_words.argtypes = [U64, U32, I64, P, I]
         lib.ig_logit_rows.argtypes = [U64, I, D, I, D, I64, I, P, P, P, I, P, I]
         lib.ig_logit_rows.restype = I
         lib.ig_sample_tokens.argtypes = [U64, U32, I64, I, I, P, P, P, P, I]
@@ -101,6 +108,51 @@ def normal(seed, stream, n):
     out = np.empty(int(n), np.float64)
     _load().ig_normal(seed, stream, int(n), _p(out), _nt())
     return out
+
+
+def words(seed, stream, n):
+    """n raw uint32 words (Philox4x32-10 outputs in counter order)."""
+    n = int(n)
+    out = np.empty(4 * ((n + 3) // 4), np.uint32)
+    _load().ig_words(seed, stream, out.size // 4, _p(out), _nt())
+    return out[:n]
+
+
+def random_bytes(seed, stream, shape):
+    n = int(np.prod(shape))
+    return words(seed, stream, (n + 3) // 4).view(np.uint8)[:n].reshape(shape)
+
+
+def acceptance_counts(seed, B, gamma, alpha):
+    """Accepted drafts per request under a fixed per-position acceptance rate alpha: the number of
+    leading successes among gamma Bernoulli(alpha) trials (0..gamma)."""
+    if gamma == 0:
+        return np.zeros(B, np.int32)
+    ok = uniform53(seed, S_ACC, B * gamma).reshape(B, gamma) < alpha
+    first_fail = np.where(ok.all(axis=1), gamma, np.argmin(ok, axis=1))
+    return first_fail.astype(np.int32)
+
+
+def kv_inputs(B, gamma, R, E, S, W, seed, *, alpha=0.8, len_hi=None):
+    """One KV commit step: staged keys and values [B, gamma+1, R, E] (random bytes), lengths
+    uniform in [0, len_hi) (default 4*(S+W): filling caches and wrapped rings), and accepted
+    counts from acceptance_counts."""
+    len_hi = 4 * (S + W) if len_hi is None else len_hi
+    return {"k_new": random_bytes(seed, S_KV, (B, gamma + 1, R, E)),
+            "v_new": random_bytes(seed + 1, S_KV, (B, gamma + 1, R, E)),
+            "lengths": np.minimum(uniform53(seed, S_LEN, B) * len_hi, len_hi - 1).astype(np.int32),
+            "num_accepted": acceptance_counts(seed, B, gamma, alpha),
+            "sink": S, "window": W, "gamma": gamma, "rows": R, "row_bytes": E}
+
+
+def window_inputs(B, W, block, K, full_cols, seed, *, len_hi=None):
+    """One draft-window step: lengths uniform in [0, len_hi] (default the full table's tokens) and a
+    full block table [B, full_cols] of distinct block ids (a seeded permutation, from 1)."""
+    len_hi = full_cols * block if len_hi is None else len_hi
+    perm = np.argsort(words(seed, S_TABLE, B * full_cols), kind="stable")
+    return {"seq_lens": np.minimum(uniform53(seed, S_LEN, B) * (len_hi + 1), len_hi).astype(np.int32),
+            "block_table": (perm.reshape(B, full_cols) + 1).astype(np.int32),
+            "window": W, "block_size": block, "future_offset": K}
 
 
 def logit_rows(seed, V, src_row, *, dist=DIST_NORMAL, scale=1.0, n_spikes=0, spike_height=0.0,
@@ -263,6 +315,8 @@ WORKLOADS = {
     "tree": dict(kind="tree", B=32, V=152064, dtype="bf16", scale=3.0, noise_sd=0.7, temperature=1.0, seed=4),
     "ragged": dict(kind="ragged", B=1024, gamma_lo=1, gamma_hi=8, V=151936, dtype="bf16", scale=3.0,
                    sigma_lo=0.2, sigma_hi=2.0, n_greedy=256, t_lo=0.5, t_hi=1.2, seed=5),
+    "kv": dict(kind="kv", B=256, gamma=5, R=256, E=256, S=4, W=1020, alpha=0.8, seed=6),
+    "window": dict(kind="window", B=256, W=2048, block=128, K=5, full_cols=320, seed=7),
 }
 
 
@@ -279,4 +333,10 @@ def make(name, seed=None, **overrides):
         return ragged_inputs(spec.pop("B"), spec.pop("gamma_lo"), spec.pop("gamma_hi"), spec.pop("V"), s, **spec)
     if kind == "tree":
         return tree_inputs(spec.pop("B"), spec.pop("V"), s, **spec)
+    if kind == "kv":
+        return kv_inputs(spec.pop("B"), spec.pop("gamma"), spec.pop("R"), spec.pop("E"), spec.pop("S"),
+                         spec.pop("W"), s, **spec)
+    if kind == "window":
+        return window_inputs(spec.pop("B"), spec.pop("W"), spec.pop("block"), spec.pop("K"), spec.pop("full_cols"),
+                             s, **spec)
     raise KeyError(kind)

@@ -181,6 +181,24 @@ static void normal_fn(void *p, int64_t lo, int64_t hi)
         ((double *)c->out)[i] = normal_at(c->seed, c->stream, 0, (uint64_t)i);
 }
 
+static void words_fn(void *p, int64_t lo, int64_t hi)
+{
+    flat_ctx *c = (flat_ctx *)p;
+    for (int64_t i = lo; i < hi; ++i) {
+        uint32_t w[4];
+        draw4(c->seed, c->stream, (uint64_t)i >> 32, (uint32_t)i, w);
+        for (int k = 0; k < 4; ++k)
+            ((uint32_t *)c->out)[4 * i + k] = w[k];
+    }
+}
+
+/* 4*n raw 32-bit words: the four outputs of counter i land at 4i .. 4i+3 */
+void ig_words(uint64_t seed, uint32_t stream, int64_t n, uint32_t *out, int nthreads)
+{
+    flat_ctx c = {seed, stream, out};
+    run(n, nthreads, words_fn, &c);
+}
+
 /* float32 uniforms on the 2^-24 grid of [0, 1 - 2^-24] */
 void ig_uniform24(uint64_t seed, uint32_t stream, int64_t n, float *out, int nthreads)
 {

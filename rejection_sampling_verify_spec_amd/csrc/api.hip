@@ -5,6 +5,7 @@
 // memory and never synchronises.
 #include "specverify.h"
 #include "sv_internal.h"
+#include "cache.h"
 
 #include <stdlib.h>
 
@@ -280,6 +281,74 @@ int spec_sample_rows(const void* logits, int32_t dtype, int32_t rows, int32_t V,
   if (launch_finish_jobs(dtype, logits, logits, V, rows, jobs, recs, part, nchunk_for(V, dtype), rows, done,
                          out_tokens, 1, force_exact_residual(), st) != hipSuccess)
     return SV_EHIP;
+  return SV_OK;
+}
+
+static bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int spec_kv_commit(void* k_cache, void* v_cache, const void* k_new, const void* v_new, const int32_t* lengths,
+                   const int32_t* num_accepted, int32_t* new_lengths, int32_t B, int32_t gamma, int32_t rows,
+                   int64_t row_bytes, int32_t sink, int32_t window, void* stream) {
+  if (B < 0 || gamma < 0 || gamma > SV_MAX_GAMMA || rows < 1 || row_bytes < 1 || row_bytes > SV_MAX_KV_ROW_BYTES ||
+      sink < 0 || window < 1 || (int64_t)sink + window > SV_MAX_KV_SLOTS)
+    return SV_EINVAL;
+  if (B == 0) return SV_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !lengths || !num_accepted || !new_lengths) return SV_EINVAL;
+  if (k_cache == v_cache || ranges_overlap(lengths, (size_t)B * 4, new_lengths, (size_t)B * 4)) return SV_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  timing_mark(st, true);
+  hipError_t e = svc::launch_kv_commit(static_cast<char*>(k_cache), static_cast<char*>(v_cache),
+                                       static_cast<const char*>(k_new), static_cast<const char*>(v_new), lengths,
+                                       num_accepted, new_lengths, B, gamma, rows, row_bytes, sink, window, st);
+  timing_mark(st, false);
+  return e == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+int spec_kv_valid_slots(const int32_t* lengths, int32_t B, int32_t sink, int32_t window, int32_t* slots,
+                        int32_t* positions, int32_t* counts, void* stream) {
+  if (B < 0 || sink < 0 || window < 1 || (int64_t)sink + window > SV_MAX_KV_SLOTS) return SV_EINVAL;
+  if (B == 0) return SV_OK;
+  if (!lengths || !slots || !counts) return SV_EINVAL;
+  return svc::launch_kv_valid_slots(lengths, B, sink, window, slots, positions, counts,
+                                    static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SV_OK
+             : SV_EHIP;
+}
+
+int32_t spec_draft_window_max_blocks(int32_t window, int32_t block_size) {
+  if (window < 1 || block_size < 1) return -1;
+  return (int32_t)(((int64_t)window + 2 * (int64_t)block_size - 2) / block_size);
+}
+
+static int check_window_args(int32_t window, int32_t block_size, int32_t future_offset) {
+  return (window < 1 || block_size < 1 || future_offset < 0 || future_offset > window) ? SV_EINVAL : SV_OK;
+}
+
+int spec_draft_window(const int32_t* seq_lens, int32_t B, int32_t window, int32_t block_size, int32_t future_offset,
+                      const int32_t* block_table, int32_t full_cols, int32_t* windowed_lens, int32_t* window_table,
+                      int32_t window_cols, void* stream) {
+  if (B < 0 || full_cols < 0 || check_window_args(window, block_size, future_offset)) return SV_EINVAL;
+  if (window_cols < spec_draft_window_max_blocks(window, block_size)) return SV_EINVAL;
+  if (B == 0) return SV_OK;
+  if (!seq_lens || !windowed_lens || !window_table || (full_cols > 0 && !block_table)) return SV_EINVAL;
+  if (seq_lens != windowed_lens && ranges_overlap(seq_lens, (size_t)B * 4, windowed_lens, (size_t)B * 4))
+    return SV_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  timing_mark(st, true);
+  hipError_t e = svc::launch_draft_window(seq_lens, B, window, block_size, future_offset, block_table, full_cols,
+                                          windowed_lens, window_table, window_cols, st);
+  timing_mark(st, false);
+  return e == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+int spec_draft_window_host(const int32_t* seq_lens, int32_t n, int32_t window, int32_t block_size,
+                           int32_t future_offset, int32_t* windowed_lens) {
+  if (n < 0 || check_window_args(window, block_size, future_offset)) return SV_EINVAL;
+  if (n > 0 && (!seq_lens || !windowed_lens)) return SV_EINVAL;
+  for (int32_t i = 0; i < n; ++i) windowed_lens[i] = svc::window_len(seq_lens[i], window, block_size, future_offset);
   return SV_OK;
 }
 

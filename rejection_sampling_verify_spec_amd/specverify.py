@@ -11,6 +11,7 @@ The convenience wrappers (``verify_chain``, ``verify_ragged``, ``verify_tree``,
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import torch
@@ -50,6 +51,17 @@ _lib.spec_sample_rows_workspace_bytes.argtypes = [_I32, _I32, _I32]
 _lib.spec_sample_rows_workspace_bytes.restype = _SZ
 _lib.spec_sample_rows.argtypes = [_P, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]
 _lib.spec_sample_rows.restype = ctypes.c_int
+_I64 = ctypes.c_int64
+_lib.spec_kv_commit.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _P]
+_lib.spec_kv_commit.restype = ctypes.c_int
+_lib.spec_kv_valid_slots.argtypes = [_P, _I32, _I32, _I32, _P, _P, _P, _P]
+_lib.spec_kv_valid_slots.restype = ctypes.c_int
+_lib.spec_draft_window_max_blocks.argtypes = [_I32, _I32]
+_lib.spec_draft_window_max_blocks.restype = _I32
+_lib.spec_draft_window.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _I32, _P, _P, _I32, _P]
+_lib.spec_draft_window.restype = ctypes.c_int
+_lib.spec_draft_window_host.argtypes = [_P, _I32, _I32, _I32, _I32, _P]
+_lib.spec_draft_window_host.restype = ctypes.c_int
 _lib.spec_verify_strerror.argtypes = [ctypes.c_int]
 _lib.spec_verify_strerror.restype = ctypes.c_char_p
 _lib.spec_verify_version.restype = ctypes.c_int
@@ -155,6 +167,31 @@ def spec_sample_rows_workspace_bytes(rows, V, dtype) -> int:
 def spec_sample_rows(logits, dtype, rows, V, temperature, u, out_tokens, workspace, workspace_bytes, stream) -> int:
     return _lib.spec_sample_rows(_ptr(logits), dtype, rows, V, _ptr(temperature), _ptr(u), _ptr(out_tokens),
                                  _ptr(workspace), workspace_bytes, stream)
+
+
+def spec_kv_commit(k_cache, v_cache, k_new, v_new, lengths, num_accepted, new_lengths, B, gamma, rows, row_bytes,
+                   sink, window, stream) -> int:
+    return _lib.spec_kv_commit(_ptr(k_cache), _ptr(v_cache), _ptr(k_new), _ptr(v_new), _ptr(lengths),
+                               _ptr(num_accepted), _ptr(new_lengths), B, gamma, rows, row_bytes, sink, window, stream)
+
+
+def spec_kv_valid_slots(lengths, B, sink, window, slots, positions, counts, stream) -> int:
+    return _lib.spec_kv_valid_slots(_ptr(lengths), B, sink, window, _ptr(slots), _ptr(positions), _ptr(counts),
+                                    stream)
+
+
+def spec_draft_window_max_blocks(window, block_size) -> int:
+    return _lib.spec_draft_window_max_blocks(window, block_size)
+
+
+def spec_draft_window(seq_lens, B, window, block_size, future_offset, block_table, full_cols, windowed_lens,
+                      window_table, window_cols, stream) -> int:
+    return _lib.spec_draft_window(_ptr(seq_lens), B, window, block_size, future_offset, _ptr(block_table), full_cols,
+                                  _ptr(windowed_lens), _ptr(window_table), window_cols, stream)
+
+
+def spec_draft_window_host(seq_lens, n, window, block_size, future_offset, windowed_lens) -> int:
+    return _lib.spec_draft_window_host(_ptr(seq_lens), n, window, block_size, future_offset, _ptr(windowed_lens))
 
 
 def spec_verify_timing_enable(enable: bool) -> int:
@@ -297,3 +334,52 @@ def sample_rows(logits, temperature, u, *, workspace=None):
     ws = workspace if workspace is not None else _ws(dev, nbytes)
     _check(spec_sample_rows(logits, dt, rows, V, temperature, u, out, ws, ws.numel(), _stream(dev)))
     return out
+
+
+def kv_commit(k_cache, v_cache, k_new, v_new, lengths, num_accepted, sink, window):
+    """Commit the kept positions of one verify step into sink + ring caches.
+
+    k_cache, v_cache [B, R, S+W, ...] (updated in place), k_new, v_new [B, gamma+1, R, ...] with the same
+    trailing shape and dtype, lengths and num_accepted int32 [B]. Returns the new lengths."""
+    B, R, cap = k_cache.shape[:3]
+    if cap != sink + window:
+        raise ValueError(f"cache has {cap} slots, sink + window = {sink + window}")
+    gamma = k_new.shape[1] - 1
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new), ("v_new", v_new)):
+        _need(t, k_cache.dtype, name)
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(v_new.shape) != tuple(k_new.shape) or \
+            tuple(k_new.shape[:1] + k_new.shape[2:3]) != (B, R) or k_new.shape[3:] != k_cache.shape[3:]:
+        raise ValueError("cache and staging shapes do not match")
+    _need(lengths, torch.int32, "lengths")
+    _need(num_accepted, torch.int32, "num_accepted")
+    row_bytes = math.prod(k_cache.shape[3:]) * k_cache.element_size()
+    out = torch.empty_like(lengths)
+    _check(spec_kv_commit(k_cache, v_cache, k_new, v_new, lengths, num_accepted, out, B, gamma, R, row_bytes, sink,
+                          window, _stream(k_cache.device)))
+    return out
+
+
+def kv_valid_slots(lengths, sink, window, *, positions=True):
+    """(slots [B, S+W], positions [B, S+W] or None, counts [B]) of sink + ring caches of these lengths."""
+    _need(lengths, torch.int32, "lengths")
+    B = lengths.shape[0]
+    dev = lengths.device
+    slots = torch.empty((B, sink + window), dtype=torch.int32, device=dev)
+    pos = torch.empty_like(slots) if positions else None
+    counts = torch.empty(B, dtype=torch.int32, device=dev)
+    _check(spec_kv_valid_slots(lengths, B, sink, window, slots, pos, counts, _stream(dev)))
+    return slots, pos, counts
+
+
+def draft_window(seq_lens, block_table, window, block_size, future_offset, *, window_cols=None):
+    """(windowed_lens [B], window_table [B, window_cols]) of a draft KV window over a full block table [B, cols]."""
+    _need(seq_lens, torch.int32, "seq_lens")
+    _need(block_table, torch.int32, "block_table")
+    B = seq_lens.shape[0]
+    dev = seq_lens.device
+    cols = window_cols if window_cols is not None else spec_draft_window_max_blocks(window, block_size)
+    lens = torch.empty(B, dtype=torch.int32, device=dev)
+    table = torch.empty((B, max(cols, 0)), dtype=torch.int32, device=dev)
+    _check(spec_draft_window(seq_lens, B, window, block_size, future_offset, block_table, block_table.shape[1], lens,
+                             table, cols, _stream(dev)))
+    return lens, table

@@ -90,3 +90,64 @@ def test_host_validation_errors(lib):
     for code in (0, -1, -2, -3, -4, -5, -99):
         assert isinstance(b.spec_verify_strerror(code), str)
     assert b.spec_verify_version() == 1
+
+
+def test_cache_entry_points_reject_bad_arguments():
+    import rejection_sampling_verify_spec_amd.specverify as b
+    d = 256
+    ok = (d, d + 4096, d, d + 8192, d + 16384, d + 20480, d + 24576)  # kc vc kn vn len nacc out
+    assert b.spec_kv_commit(*ok, -1, 5, 4, 256, 4, 60, None) == b.SV_EINVAL          # B < 0
+    assert b.spec_kv_commit(None, None, None, None, None, None, None, 0, 5, 4, 256, 4, 60, None) == b.SV_OK
+    assert b.spec_kv_commit(*ok, 2, 5, 4, 256, 4, 0, None) == b.SV_EINVAL            # W = 0
+    assert b.spec_kv_commit(*ok, 2, 5, 4, 256, -1, 8, None) == b.SV_EINVAL           # S < 0
+    assert b.spec_kv_commit(*ok, 2, 5, 0, 256, 4, 8, None) == b.SV_EINVAL            # no rows
+    assert b.spec_kv_commit(*ok, 2, 5, 4, 0, 4, 8, None) == b.SV_EINVAL              # empty rows
+    assert b.spec_kv_commit(*ok, 2, 257, 4, 256, 4, 8, None) == b.SV_EINVAL          # gamma too large
+    assert b.spec_kv_commit(*ok, 2, 5, 4, 256, 1 << 29, (1 << 29) + 1, None) == b.SV_EINVAL  # S + W too large
+    assert b.spec_kv_commit(d, d, *ok[2:], 2, 5, 4, 256, 4, 8, None) == b.SV_EINVAL  # k_cache == v_cache
+    bad = list(ok)
+    bad[6] = ok[4] + 4  # new_lengths overlaps lengths
+    assert b.spec_kv_commit(*bad, 2, 5, 4, 256, 4, 8, None) == b.SV_EINVAL
+    bad[6] = None
+    assert b.spec_kv_commit(*bad, 2, 5, 4, 256, 4, 8, None) == b.SV_EINVAL
+    assert b.spec_kv_valid_slots(d, 2, 4, 0, d, None, d, None) == b.SV_EINVAL
+    assert b.spec_kv_valid_slots(d, 2, 4, 8, None, None, d, None) == b.SV_EINVAL
+    assert b.spec_kv_valid_slots(None, 0, 4, 8, None, None, None, None) == b.SV_OK
+    # draft window: block bound, K above W, zero block size, short clone width
+    assert b.spec_draft_window_max_blocks(64, 16) == 5 and b.spec_draft_window_max_blocks(63, 16) == 5
+    assert b.spec_draft_window_max_blocks(2048, 128) == 17 and b.spec_draft_window_max_blocks(0, 16) == -1
+    args = dict(seq=d, B=4, W=64, b=16, K=3, table=d + 64, cols=20, out=d + 4096, win=d + 8192, wc=5)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return b.spec_draft_window(a["seq"], a["B"], a["W"], a["b"], a["K"], a["table"], a["cols"], a["out"],
+                                   a["win"], a["wc"], None)
+    assert call(wc=4) == b.SV_EINVAL
+    assert call(K=65) == b.SV_EINVAL
+    assert call(b=0, wc=100) == b.SV_EINVAL
+    assert call(B=-1) == b.SV_EINVAL
+    assert call(B=0) == b.SV_OK
+    assert call(table=None) == b.SV_EINVAL
+    assert call(out=d + 4) == b.SV_EINVAL  # overlaps seq_lens without being it
+
+
+def test_draft_window_host_matches_oracle():
+    """The host-side windowed length (for host copies of the length inputs) runs here without a GPU."""
+    import numpy as np
+
+    import oracle
+    import rejection_sampling_verify_spec_amd.specverify as b
+    rng = np.random.default_rng(12)
+    for W, bs, K in [(64, 16, 3), (63, 16, 0), (2048, 128, 5), (7, 3, 7), (1, 1, 0), (100, 7, 50)]:
+        seq = np.concatenate([np.arange(-3, 4 * W + 3 * bs), rng.integers(0, 2 ** 31 - 1, 200),
+                              [2 ** 31 - 1, -(2 ** 31)]]).astype(np.int32)
+        out = np.empty_like(seq)
+        assert b.spec_draft_window_host(seq.ctypes.data, seq.size, W, bs, K, out.ctypes.data) == b.SV_OK
+        ref = [(-1 if oracle.window_one(int(L), W, bs, K) is None else oracle.window_one(int(L), W, bs, K)[1])
+               for L in seq]
+        assert out.tolist() == ref
+        # in place
+        assert b.spec_draft_window_host(seq.ctypes.data, seq.size, W, bs, K, seq.ctypes.data) == b.SV_OK
+        assert seq.tolist() == ref
+    assert b.spec_draft_window_host(None, 0, 64, 16, 3, None) == b.SV_OK
+    assert b.spec_draft_window_host(None, 3, 64, 16, 3, None) == b.SV_EINVAL

@@ -94,3 +94,24 @@ def test_workload_shapes():
     pos = r["temperature"][r["temperature"] > 0]
     assert pos.min() >= 0.5 and pos.max() <= 1.2
     assert r["target"].shape == (r["total_draft"] + 1024, 16)
+
+
+def test_words_are_philox_outputs_in_counter_order():
+    w = inputgen.words(9, inputgen.S_KV, 10)
+    ref = [inputgen.philox4x32_10([i, 0, 0, inputgen.S_KV], [9, 0]).tolist() for i in range(3)]
+    assert w.tolist() == (ref[0] + ref[1] + ref[2])[:10]
+
+
+def test_kv_and_window_workloads():
+    d = inputgen.kv_inputs(16, 5, 3, 10, 4, 12, 1)
+    assert d["k_new"].shape == (16, 6, 3, 10) and d["k_new"].dtype == np.uint8
+    assert not np.array_equal(d["k_new"], d["v_new"])
+    assert ((d["lengths"] >= 0) & (d["lengths"] < 64)).all()
+    assert ((d["num_accepted"] >= 0) & (d["num_accepted"] <= 5)).all()
+    n = inputgen.acceptance_counts(3, 200000, 5, 0.8)
+    # P(n = k) = 0.8^k * 0.2 for k < 5, 0.8^5 for k = 5
+    p = np.array([0.8 ** k * 0.2 for k in range(5)] + [0.8 ** 5])
+    assert np.allclose(np.bincount(n, minlength=6) / n.size, p, atol=0.005)
+    w = inputgen.window_inputs(8, 64, 16, 3, 12, 2)
+    assert w["block_table"].shape == (8, 12) and len(np.unique(w["block_table"])) == 96
+    assert ((w["seq_lens"] >= 0) & (w["seq_lens"] <= 192)).all()
