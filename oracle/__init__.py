@@ -22,6 +22,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
 MUT_NONE, MUT_LOGIT_RESIDUAL, MUT_RESAMPLE_TARGET, MUT_ALWAYS_ACCEPT, MUT_NO_BONUS = range(5)
+MUT_TREE_NO_UPDATE, MUT_TREE_NO_RENORM = 5, 6
 
 _lib = None
 
@@ -49,6 +50,8 @@ def _load():
         lib.oracle_verify_chain.restype = I
         lib.oracle_verify_tree.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, P, P, P, P, P, I]
         lib.oracle_verify_tree.restype = I
+        lib.oracle_verify_tree_lossless.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, P, P, P, P, P, I, I]
+        lib.oracle_verify_tree_lossless.restype = I
         lib.oracle_row_stats.argtypes = [P, I, I, I, P, P, P, P, P, I]
         lib.oracle_row_stats.restype = I
         lib.oracle_sample_rows.argtypes = [P, I, I, I, P, P, P, P, I]
@@ -142,6 +145,33 @@ def verify_tree(target, draft, node_tokens, parents, u_accept, u_sample, tempera
                                     _ptr(na), _ptr(am), _ptr(cm), _threads(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_verify_tree failed")
+    return dict(out_tokens=out, out_nodes=onodes, num_accepted=na, acc_margin=am, cdf_margin=cm)
+
+
+def verify_tree_lossless(target, draft, node_tokens, parents, u_accept, u_sample, temperature, max_depth,
+                         nthreads=None, mutant=MUT_NONE):
+    """Lossless multi-candidate token-tree verification (siblings tried in index order, each
+    against the residual left by the rejected ones). Same arguments and outputs as verify_tree."""
+    target, dt = _logits(target)
+    draft, dt2 = _logits(draft)
+    assert dt == dt2
+    temperature = np.ascontiguousarray(temperature, dtype=np.float32)
+    B, N, V = target.shape
+    tok = np.ascontiguousarray(node_tokens, dtype=np.int32)
+    par = np.ascontiguousarray(parents, dtype=np.int32)
+    ua = np.ascontiguousarray(u_accept, dtype=np.float32)
+    us = np.ascontiguousarray(u_sample, dtype=np.float32)
+    out = np.empty((B, max_depth + 1), np.int32)
+    onodes = np.empty((B, max_depth + 1), np.int32)
+    na = np.empty(B, np.int32)
+    am = np.empty(B, np.float64)
+    cm = np.empty(B, np.float64)
+    rc = _load().oracle_verify_tree_lossless(_ptr(target), _ptr(draft), dt, _ptr(tok), _ptr(par), _ptr(ua),
+                                             _ptr(us), _ptr(temperature), B, N, V, int(max_depth), _ptr(out),
+                                             _ptr(onodes), _ptr(na), _ptr(am), _ptr(cm), int(mutant),
+                                             _threads(nthreads))
+    if rc != 0:
+        raise RuntimeError("oracle_verify_tree_lossless failed")
     return dict(out_tokens=out, out_nodes=onodes, num_accepted=na, acc_margin=am, cdf_margin=cm)
 
 

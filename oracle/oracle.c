@@ -58,6 +58,8 @@
 #define MUT_RESAMPLE_TARGET 2 /* on rejection resample from P_t instead of P' */
 #define MUT_ALWAYS_ACCEPT 3  /* accept every draft token */
 #define MUT_NO_BONUS 4       /* all drafts accepted: resample last draft row's P_t instead of the bonus row */
+#define MUT_TREE_NO_UPDATE 5  /* lossless tree: siblings all tested against P_t, draw against the first child */
+#define MUT_TREE_NO_RENORM 6  /* lossless tree: the residual after a rejected sibling is not renormalised */
 
 /* ------------------------------------------------------------------------ */
 /* Input decoding: exact widening to double.                                 */
@@ -489,6 +491,7 @@ typedef struct {
     int B, N, V, max_depth;
     int32_t *out, *out_nodes, *num_accepted;
     double *acc_margin, *cdf_margin;
+    int mutant;
 } tree_batch;
 
 static void tree_task(void *p, int b, double *work)
@@ -630,6 +633,168 @@ int oracle_verify_tree(const void *target, const void *draft, int dtype, const i
                      num_accepted, acc_margin, cdf_margin};
     size_t work = 2 * (size_t)N + (size_t)(2 * N + 1) * (size_t)V;
     return run_parallel(B, nthreads, work, tree_task, &tb);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Lossless multi-candidate token-tree verification.  The tree layout, the
+ * validation and the row conventions are those of oracle_verify_tree.  At the
+ * current node v (from the root) the current distribution is r = P_t[v]; the
+ * children of v are tried in ascending index order, each with the acceptance
+ * rule of [Primer 考点2] against r: child c is accepted when
+ * u_accept[c] * P_d[c](x_c) < r(x_c).  An accepted child becomes the current
+ * node.  A rejected child replaces r by its residual max(0, r - P_d[c]) / sum
+ * [Primer 考点2, P'] before the next sibling is tried; a residual whose sum
+ * underflows to 0 leaves r unchanged.  When no child is accepted (or v has no
+ * children) the final token is drawn from r with u_sample[v] by the inverse
+ * CDF.  Each step's output then follows P_t whatever the draft rows are, as
+ * long as each child's token was drawn from its own draft row independently of
+ * the others.  Greedy (T == 0): the first child whose token is the argmax of
+ * P_t[v] is accepted; otherwise the argmax is emitted.                      */
+
+static void tree_lossless_task(void *p, int b, double *work)
+{
+    const tree_batch *tb = (const tree_batch *)p;
+    const int N = tb->N, V = tb->V, width = tb->max_depth + 1;
+    int32_t *out = tb->out + (size_t)b * width, *onodes = tb->out_nodes + (size_t)b * width;
+    const int32_t *par = tb->parents + (size_t)b * N, *tok = tb->tokens + (size_t)b * N;
+    const float *ua = tb->ua + (size_t)b * N, *us = tb->us + (size_t)b * N;
+    const float Tf = tb->temperature[b];
+    const size_t t0 = (size_t)b * N, d0 = (size_t)b * (N - 1);
+    tb->acc_margin[b] = INFINITY;
+    tb->cdf_margin[b] = INFINITY;
+    for (int k = 0; k < width; ++k)
+        onodes[k] = -1;
+
+    int *depth = (int *)(work);
+    int *amax = depth + N;
+    double *dwork = work + 2 * (size_t)N;
+
+    int ok = temperature_usable(Tf) && par[0] == -1;
+    depth[0] = 0;
+    for (int v = 1; ok && v < N; ++v) {
+        if (par[v] < 0 || par[v] >= v) {
+            ok = 0;
+            break;
+        }
+        depth[v] = depth[par[v]] + 1;
+        if (depth[v] > tb->max_depth)
+            ok = 0;
+        if (tok[v] < 0 || tok[v] >= V)
+            ok = 0;
+    }
+    if (ok && Tf > 0.0f) {
+        for (int v = 1; ok && v < N; ++v)
+            ok = uniform_usable(ua[v]);
+        for (int v = 0; ok && v < N; ++v)
+            ok = uniform_usable(us[v]);
+    }
+    for (int v = 0; ok && v < N; ++v)
+        ok = row_usable(tb->target, tb->dtype, (t0 + v) * (size_t)V, V);
+    if (ok && Tf > 0.0f)
+        for (int v = 1; ok && v < N; ++v)
+            ok = row_usable(tb->draft, tb->dtype, (d0 + v - 1) * (size_t)V, V);
+    if (!ok) {
+        fail_request(out, width, tb->num_accepted + b);
+        return;
+    }
+    for (int k = 0; k < width; ++k)
+        out[k] = -1;
+
+    int v = 0, d = 0;
+    if (Tf == 0.0f) {
+        for (int w = 0; w < N; ++w)
+            amax[w] = argmax_row(tb->target, tb->dtype, (t0 + w) * (size_t)V, V);
+        for (;;) {
+            int next = -1;
+            for (int c = 1; c < N; ++c)
+                if (par[c] == v && tok[c] == amax[v]) {
+                    next = c;
+                    break;
+                }
+            if (next < 0)
+                break;
+            out[d] = tok[next];
+            onodes[d] = next;
+            ++d;
+            v = next;
+        }
+        out[d] = amax[v];
+        tb->num_accepted[b] = d;
+        return;
+    }
+
+    const double T = (double)Tf;
+    double *r = dwork;        /* [V] current distribution */
+    double *q = r + V;        /* [V] draft distribution of the child under test */
+    double *res = q + V;      /* [V] residual */
+    double *first = res + V;  /* [V] draft distribution of the first child (planted mistake) */
+    for (;;) {
+        softmax_row(tb->target, tb->dtype, (t0 + v) * (size_t)V, V, T, r, NULL, NULL);
+        int accepted = -1, nrej = 0;
+        for (int c = 1; c < N; ++c) {
+            if (par[c] != v)
+                continue;
+            softmax_row(tb->draft, tb->dtype, (d0 + c - 1) * (size_t)V, V, T, q, NULL, NULL);
+            const int x = tok[c];
+            const double Pt = r[x], Pd = q[x];
+            double ratio = Pd > 0.0 ? fmin(1.0, Pt / Pd) : (Pt > 0.0 ? 1.0 : 0.0);
+            double dm = fabs((double)ua[c] - ratio);
+            if (dm < tb->acc_margin[b])
+                tb->acc_margin[b] = dm;
+            if ((double)ua[c] * Pd < Pt) {
+                accepted = c;
+                break;
+            }
+            if (nrej++ == 0)
+                memcpy(first, q, (size_t)V * sizeof(double));
+            if (tb->mutant == MUT_TREE_NO_UPDATE)
+                continue;
+            double Z = 0.0;
+            for (int j = 0; j < V; ++j) {
+                res[j] = fmax(0.0, r[j] - q[j]);
+                Z += res[j];
+            }
+            if (Z > 0.0)
+                for (int j = 0; j < V; ++j)
+                    r[j] = tb->mutant == MUT_TREE_NO_RENORM ? res[j] : res[j] / Z;
+        }
+        if (accepted < 0) {
+            if (tb->mutant == MUT_TREE_NO_UPDATE && nrej > 0) {
+                double Z = 0.0;
+                for (int j = 0; j < V; ++j) {
+                    res[j] = fmax(0.0, r[j] - first[j]);
+                    Z += res[j];
+                }
+                if (Z > 0.0)
+                    memcpy(r, res, (size_t)V * sizeof(double));
+            }
+            break;
+        }
+        out[d] = tok[accepted];
+        onodes[d] = accepted;
+        ++d;
+        v = accepted;
+    }
+    double margin;
+    out[d] = inverse_cdf(r, V, (double)us[v], &margin);
+    tb->cdf_margin[b] = margin;
+    tb->num_accepted[b] = d;
+}
+
+/* Same arguments as oracle_verify_tree, plus a planted-mistake selector. */
+int oracle_verify_tree_lossless(const void *target, const void *draft, int dtype, const int32_t *tokens,
+                                const int32_t *parents, const float *u_accept, const float *u_sample,
+                                const float *temperature, int B, int N, int V, int max_depth, int32_t *out,
+                                int32_t *out_nodes, int32_t *num_accepted, double *acc_margin, double *cdf_margin,
+                                int mutant, int nthreads)
+{
+    if (B < 0 || N < 1 || V < 1 || max_depth < 0 || (dtype != OR_F32 && dtype != OR_BF16))
+        return -1;
+    tree_batch tb = {target,      draft,      dtype,     tokens, parents,   u_accept,     u_sample,
+                     temperature, B,          N,         V,      max_depth, out,          out_nodes,
+                     num_accepted, acc_margin, cdf_margin, mutant};
+    size_t work = 2 * (size_t)N + 4 * (size_t)V;
+    return run_parallel(B, nthreads, work, tree_lossless_task, &tb);
 }
 
 /* ------------------------------------------------------------------------ */
