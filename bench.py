@@ -44,6 +44,7 @@ WORKLOAD_TEXT = {
     "tiny": "tiny chain verify: B=8, gamma=4, V=256, fp32",
     "mid": "mid chain verify: B=64, gamma=5, V=32000, fp32, 20 spikes +8, T=0.8",
     "tree": "token-tree verify: B=32, 64 nodes, V=152064, bf16",
+    "tree_lossless": "lossless multi-candidate token-tree verify: B=32, 64 nodes, V=152064, bf16",
     "ragged": "ragged mixed verify: B=1024, gamma_b in 1..8, V=151936, bf16, 256 greedy",
     "sample": "draft-token sampling: one token per row of the large workload's 1280 draft rows "
               "(V=128256, bf16, Student-t), T=1.0",
@@ -62,6 +63,8 @@ def make_inputs(name):
     import numpy as np
 
     import inputgen
+    if name == "tree_lossless":
+        return inputgen.make("tree")
     if name == "sample":
         d = inputgen.make("large")
         rows = np.ascontiguousarray(d["draft"].reshape(-1, d["draft"].shape[-1]))
@@ -114,7 +117,7 @@ def workload_accounting(name, d):
     V = d["target"].shape[-1]
     T = d["temperature"]
     B = T.shape[0]
-    if name == "tree":
+    if name in ("tree", "tree_lossless"):
         N = d["target"].shape[1]
         positions = B * (N - 1)
         formula = B * (2 * N - 1) * V * es + B * V * es
@@ -132,10 +135,37 @@ def workload_accounting(name, d):
     return positions, formula, rows_read * V * es
 
 
+def lossless_walk_bytes(d, out_nodes, num_accepted):
+    """Logit bytes the lossless tree walk reads in its passes, from the walk's own outputs: at each
+    node of the emitted path, every sibling rejected before the accepted child (all children at the
+    end node) costs one pass over the node's target row and the draft rows of the siblings rejected
+    so far; an end node with no rejected child costs one pass over its target row."""
+    import numpy as np
+    B, N, V = d["target"].shape
+    es = 2 if d["target"].dtype == np.uint16 else 4
+    rows = 0
+    for b in range(B):
+        na = int(num_accepted[b])
+        if na < 0 or d["temperature"][b] == 0.0:
+            continue
+        par = d["parents"][b]
+        path = [0] + [int(x) for x in out_nodes[b, :na]]
+        for i, v in enumerate(path):
+            kids = [c for c in range(1, N) if par[c] == v]
+            k = len(kids) if i == len(path) - 1 else sum(1 for c in kids if c < path[i + 1])
+            rows += sum(1 + j for j in range(1, k + 1))
+            if i == len(path) - 1 and k == 0:
+                rows += 1
+    return rows * V * es
+
+
 def make_call(sv, name, t, d):
     """Closure running one verify step on device tensors t."""
     if name == "sample":
         return lambda tt: sv.sample_rows(tt["logits"], tt["temperature"], tt["u"])
+    if name == "tree_lossless":
+        return lambda tt: sv.verify_tree_lossless(tt["target"], tt["draft"], tt["node_tokens"], tt["parents"],
+                                                  tt["u_accept"], tt["u_sample"], tt["temperature"], d["max_depth"])
     if name == "tree":
         return lambda tt: sv.verify_tree(tt["target"], tt["draft"], tt["node_tokens"], tt["parents"],
                                          tt["u_accept"], tt["u_sample"], tt["temperature"], d["max_depth"])
@@ -151,6 +181,9 @@ def oracle_call(name, d, nthreads):
     import oracle
     if name == "sample":
         return oracle.sample_rows(d["logits"], d["temperature"], d["u"], nthreads=nthreads)
+    if name == "tree_lossless":
+        return oracle.verify_tree_lossless(d["target"], d["draft"], d["node_tokens"], d["parents"], d["u_accept"],
+                                           d["u_sample"], d["temperature"], d["max_depth"], nthreads=nthreads)
     if name == "tree":
         return oracle.verify_tree(d["target"], d["draft"], d["node_tokens"], d["parents"], d["u_accept"],
                                   d["u_sample"], d["temperature"], d["max_depth"], nthreads=nthreads)
@@ -382,6 +415,9 @@ def run_bench(args):
     ms_per_step = elapsed * 1e3 / args.steps
     value = positions * args.steps / elapsed
     gbps = formula_bytes * args.steps / elapsed / 1e9
+    walk_ms = None
+    if name == "tree_lossless":  # two event pairs per call: the streaming kernel, then the walk
+        walk_ms, k1_ms = k1_ms[1::2], k1_ms[0::2]
     k1_avg_ms = float(np.mean(k1_ms)) if k1_ms else float("nan")
     k1_gbps = k1_bytes / (k1_avg_ms * 1e-3) / 1e9
 
@@ -457,6 +493,18 @@ def run_bench(args):
     }
     if not sample:
         line["mean_num_accepted"] = round(float(np.mean(na[na >= 0])), 4)
+    if walk_ms:
+        # the walk kernel takes most of the step: its passes are latency-bound, the streaming
+        # kernel's entry moves to row_stats_roofline
+        walk_avg = float(np.mean(walk_ms))
+        wb = lossless_walk_bytes(d, outs[1].cpu().numpy(), na)
+        line["row_stats_roofline"] = line["roofline"]
+        line["roofline"] = {
+            "bound": "hbm", "kernel": "k_tree_lossless", "achieved": round(wb / (walk_avg * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(wb / (walk_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "traffic": None, "algorithmic_bytes_per_launch": wb, "avg_launch_ms": round(walk_avg, 5),
+            "launches_timed": len(walk_ms), "timed_every_nth_step": args.time_every,
+        }
     print(json.dumps(line), flush=True)
     return 0 if parity_ok is not False else 1
 

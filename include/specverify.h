@@ -157,6 +157,37 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int32_
                      int32_t max_depth, int32_t* out_tokens, int32_t* out_nodes, int32_t* num_accepted,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes for spec_verify_tree_lossless. */
+size_t spec_verify_tree_lossless_workspace_bytes(int32_t B, int32_t N, int32_t V, int32_t dtype);
+
+/*
+ * Lossless multi-candidate token-tree verification [Primer 考点3: a token
+ * tree verified in one target pass; Primer 考点2: acceptance
+ * min(1, p_target/p_draft) and the residual max(0, p_target - p_draft)/sum].
+ * Same tree layout, arguments, outputs and error reports as spec_verify_tree;
+ * only the walk differs. From the root, the current distribution r is the
+ * current node's target row; its children are tried in ascending index order:
+ * child c is accepted when u_accept[c] * p_draft[c](x_c) < r(x_c) and then
+ * becomes the current node; a rejected child replaces r by
+ * max(0, r - p_draft[c]) / sum before its next sibling is tried (a sum that
+ * underflows to 0 keeps r). When no child is accepted, or the node is a leaf,
+ * the final token is drawn from r with u_sample of that node by the inverse
+ * CDF (y = min{ j : C_j > u*S }). Each emitted token then follows the target
+ * distribution exactly, provided each child's token was drawn from its own
+ * draft row independently of its siblings. Greedy requests (T == 0) follow the
+ * first child whose token is the argmax of the current node's target row and
+ * emit the argmax at the end.
+ * A rejection costs one pass over the current target row and the draft rows of
+ * the rejected siblings. The call runs as a cooperative launch (every
+ * workgroup resident at once); it returns SV_EHIP if the device cannot launch
+ * it.
+ */
+int spec_verify_tree_lossless(const void* target_logits, const void* draft_logits, int32_t dtype,
+                              const int32_t* node_tokens, const int32_t* parents, const float* u_accept,
+                              const float* u_sample, const float* temperature, int32_t B, int32_t N, int32_t V,
+                              int32_t max_depth, int32_t* out_tokens, int32_t* out_nodes, int32_t* num_accepted,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes for spec_row_softmax_stats. */
 size_t spec_row_softmax_stats_workspace_bytes(int32_t rows, int32_t V, int32_t dtype);
 
@@ -306,9 +337,10 @@ int spec_verify_version(void);
 
 /*
  * Optional timing of the streaming row-statistics kernel inside the calls
- * above (in spec_kv_commit and spec_draft_window: of their one kernel). While
- * recording is on, each call records a pair of HIP events around that kernel
- * on `stream`. spec_verify_timing_enable(1) starts or resumes recording,
+ * above (in spec_kv_commit and spec_draft_window: of their one kernel;
+ * spec_verify_tree_lossless records two pairs, the streaming kernel's and then
+ * the tree walk's). While recording is on, each call records a pair of HIP
+ * events around that kernel on `stream`. spec_verify_timing_enable(1) starts or resumes recording,
  * spec_verify_timing_enable(0) pauses it (recorded pairs are kept),
  * spec_verify_timing_reset() forgets them. spec_verify_timing_read returns the
  * recorded per-call durations (ms), after the caller synchronised the stream;

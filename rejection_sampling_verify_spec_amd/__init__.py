@@ -11,6 +11,7 @@ from .specverify import (  # noqa: F401
     spec_row_softmax_stats_workspace_bytes, spec_verify, spec_verify_ragged, spec_verify_ragged_workspace_bytes,
     spec_verify_strerror, spec_verify_timing_enable, spec_verify_timing_read,
     spec_verify_timing_reset, spec_verify_tree,
+    spec_verify_tree_lossless, spec_verify_tree_lossless_workspace_bytes,
     spec_verify_tree_workspace_bytes, spec_verify_version, spec_verify_workspace_bytes, verify_chain, verify_ragged,
-    verify_tree,
+    verify_tree, verify_tree_lossless,
 )

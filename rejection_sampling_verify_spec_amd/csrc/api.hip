@@ -15,6 +15,14 @@
 
 using namespace sv;
 
+namespace sv {
+hipError_t launch_tree_lossless(int dt, const void* tgt, const void* dft, int V, const Layout& L, int max_depth,
+                                const int32_t* tokens, const int32_t* parents, const float* ua, const float* us,
+                                const float* temperature, const Partial* part, int nchunk, double* tiles, int* ctr,
+                                int32_t* out, int32_t* out_nodes, int32_t* num_acc, hipStream_t st);
+int lossless_segments(int V, int dt);
+}  // namespace sv
+
 static_assert(sizeof(Partial) == 8, "Partial layout");
 static_assert(sizeof(TileRec) == 128, "TileRec layout");
 
@@ -139,6 +147,25 @@ size_t spec_verify_tree_workspace_bytes(int32_t B, int32_t N, int32_t V, int32_t
   return carve((long long)B * (2 * N - 1), B, V, dtype).total;
 }
 
+// Lossless tree workspace: row-chunk partials | per-team segment sums (two
+// buffers) | per-team counters.
+struct CarveLL {
+  size_t part, sums, ctr, total;
+};
+static CarveLL carve_ll(int B, int N, int V, int dt) {
+  CarveLL c;
+  c.part = 0;
+  c.sums = align256((size_t)B * (2 * N - 1) * nchunk_for(V, dt) * sizeof(Partial));
+  c.ctr = c.sums + align256((size_t)B * 2 * lossless_segments(V, dt) * sizeof(double));
+  c.total = c.ctr + align256((size_t)B * sizeof(int));
+  return c;
+}
+
+size_t spec_verify_tree_lossless_workspace_bytes(int32_t B, int32_t N, int32_t V, int32_t dtype) {
+  if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES || V < 1 || V > SV_MAX_VOCAB || (dtype != 0 && dtype != 1)) return 0;
+  return carve_ll(B, N, V, dtype).total;
+}
+
 size_t spec_sample_rows_workspace_bytes(int32_t rows, int32_t V, int32_t dtype) {
   if (rows < 0 || V < 1 || V > SV_MAX_VOCAB || (dtype != 0 && dtype != 1)) return 0;
   return carve(rows, rows, V, dtype).total;
@@ -235,6 +262,37 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int32_
                          out_tokens, max_depth + 1, force_exact_residual(), st) != hipSuccess)
     return SV_EHIP;
   return SV_OK;
+}
+
+int spec_verify_tree_lossless(const void* target_logits, const void* draft_logits, int32_t dtype,
+                              const int32_t* node_tokens, const int32_t* parents, const float* u_accept,
+                              const float* u_sample, const float* temperature, int32_t B, int32_t N, int32_t V,
+                              int32_t max_depth, int32_t* out_tokens, int32_t* out_nodes, int32_t* num_accepted,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || N < 1 || N > SV_MAX_TREE_NODES || max_depth < 0 || max_depth >= N) return SV_EINVAL;
+  if (B == 0) return SV_OK;
+  int rc = check_common(target_logits, draft_logits, N > 1, dtype, V);
+  if (rc) return rc;
+  if (!node_tokens || !parents || !u_accept || !u_sample || !temperature || !out_tokens || !out_nodes ||
+      !num_accepted)
+    return SV_EINVAL;
+  const long long RT = (long long)B * N, RD = (long long)B * (N - 1);
+  const CarveLL cv = carve_ll(B, N, V, dtype);
+  rc = check_ws(workspace, workspace_bytes, cv.total);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  Partial* part = reinterpret_cast<Partial*>(ws + cv.part);
+  double* sums = reinterpret_cast<double*>(ws + cv.sums);
+  int* ctr = reinterpret_cast<int*>(ws + cv.ctr);
+  Layout L{LAYOUT_TREE, B, N, nullptr, 0, RT, RD};
+  if ((rc = launch_stats(dtype, target_logits, draft_logits, V, L, temperature, part, st, ctr))) return rc;
+  timing_mark(st, true);
+  const hipError_t e = launch_tree_lossless(dtype, target_logits, draft_logits, V, L, max_depth, node_tokens, parents,
+                                            u_accept, u_sample, temperature, part, nchunk_for(V, dtype), sums, ctr,
+                                            out_tokens, out_nodes, num_accepted, st);
+  timing_mark(st, false);
+  return e == hipSuccess ? SV_OK : SV_EHIP;
 }
 
 int spec_row_softmax_stats(const void* logits, int32_t dtype, int32_t rows, int32_t V, const float* temperature,

@@ -1,0 +1,572 @@
+// tree_lossless.hip -- lossless multi-candidate token-tree verification.
+//
+// The tree of drafted tokens is verified in one target pass [Primer 考点3]; at
+// the current node (from the root) the children are tried in ascending index
+// order against the current distribution r, which starts as the node's target
+// row: child c is accepted when u_accept[c] * p_d[c](x_c) < r(x_c) [Primer
+// 考点2]. An accepted child becomes the current node. A rejected child replaces
+// r by its residual max(0, r - p_d[c]) / sum [Primer 考点2, P'] before the next
+// sibling is tried, which keeps every step's output distributed as the target
+// row. When no child is accepted (or the node is a leaf) the final token is
+// drawn from r by the inverse CDF with u_sample of the node.
+//
+// In unnormalised form, with R_0 = p_t[v] and S_0 = 1,
+//   R_{i+1}(y) = max(0, R_i(y) - S_i p_d[c_i](y)),   S_{i+1} = sum_y R_{i+1}(y),
+// so r = R_i / S_i after i rejected siblings, and child c_i is accepted when
+// u * p_d[c_i](x) * S_i < R_i(x). Each rejection needs one full-vocabulary sum:
+// a pass over the target row and the draft rows of the rejected siblings.
+//
+// One cooperative launch: a team of G workgroups per request (teams loop over
+// requests). Every workgroup of a team walks the tree redundantly (the same
+// inputs give the same decisions); a pass splits the row's segments (64
+// vectors of 16 bytes) over the team's waves, each segment's sum of R is
+// stored with a device-scope store, and the team meets at a counter (the
+// launch keeps every workgroup resident, so the wait ends; it is also
+// bounded). Each workgroup then sums the segment sums in the same fixed order.
+// The first workgroup of the team writes the outputs and, at the end, picks
+// the token inside the segment that holds u * S.
+#include "accept.h"
+#include "tail.h"
+
+namespace sv {
+
+constexpr int kLLWaves = 4;
+constexpr int kLLThreads = kLLWaves * 64;
+constexpr int kLLMaxNodes = SV_MAX_TREE_NODES;
+constexpr int kSpinPolls = 1 << 24;  // bound of one team wait (a few seconds of polls)
+
+struct LLArgs {
+  const void* tgt;
+  const void* dft;
+  int V, N, B, max_depth;
+  const int32_t* tokens;
+  const int32_t* parents;
+  const float* ua;
+  const float* us;
+  const float* temperature;
+  const Partial* part;
+  int nchunk;
+  long long RT;      // rows of the target array (draft partials follow)
+  double* sums;      // [nteams][2][nseg] segment sums, double-buffered over passes
+  int* ctr;          // [nteams] passes completed x G, zero at launch
+  int G, nteams, nseg;
+  int32_t* out;
+  int32_t* out_nodes;
+  int32_t* num_acc;
+};
+
+struct LLSpace {
+  int par[kLLMaxNodes], tok[kLLMaxNodes], idx[kLLMaxNodes];
+  int depth[2][kLLMaxNodes];
+  float mt[kLLMaxNodes], md[kLLMaxNodes];
+  double zt[kLLMaxNodes], zd[kLLMaxNodes];
+  int kids[kLLMaxNodes];  // children of the current node, ascending
+  int rej[kLLMaxNodes];   // its rejected children, in order
+  int skip[kLLMaxNodes];  // 1 when that rejection's residual sum underflowed (r kept)
+  double S[kLLMaxNodes + 1];
+  double tm[kLLMaxNodes + 1];  // masses at the token under test: target row, rejected siblings, the child
+  double tab[64];
+  int cnt[kLLWaves];
+  int bad, flag, nk, wait_ok;
+};
+
+__device__ __forceinline__ uint64_t f64_bits(double v) { return (uint64_t)__double_as_longlong(v); }
+
+// Segment sums of pass buffer `buf` read by one wave, kSegLoads per lane at a
+// time with all loads in flight: lane l holds segments l + 64 k at v[k].
+constexpr int kSegLoads = 8;
+__device__ __forceinline__ void load_segments(const double* buf, int nseg, int k0, int lane,
+                                              double (&v)[kSegLoads]) {
+#pragma unroll
+  for (int k = 0; k < kSegLoads; ++k) {
+    const int t = (k0 + k) * 64 + lane;
+    v[k] = t < nseg ? __longlong_as_double((long long)__hip_atomic_load(
+                          reinterpret_cast<uint64_t*>(const_cast<double*>(buf)) + t, __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT))
+                    : 0.0;
+  }
+}
+
+// Sum over the segments of pass buffer `buf`, in one fixed order (lane l adds
+// segments l, l + 64, ... in turn; then the wave sum): the same value in every
+// workgroup.
+__device__ __forceinline__ double sum_segments(const double* buf, int nseg, int lane) {
+  double s = 0.0;
+  for (int k0 = 0; k0 * 64 < nseg; k0 += kSegLoads) {
+    double v[kSegLoads];
+    load_segments(buf, nseg, k0, lane, v);
+#pragma unroll
+    for (int k = 0; k < kSegLoads; ++k) s += v[k];
+  }
+  return wave_sum(s);
+}
+
+// The acceptance test of child c of node v after nrej rejected siblings: wave 0
+// loads the token's logit in the target row, in each rejected sibling's draft
+// row and in c's draft row at once and forms their probabilities; thread 0
+// then applies the residual steps in order and compares (result in P.flag).
+template <int DT>
+__device__ __forceinline__ void child_test(const LLArgs& A, LLSpace& P, long long t0, long long d0, int v, int nrej,
+                                           int c, double c64, float c32) {
+  const int tid = threadIdx.x;
+  const int x = P.tok[c];
+  if (tid < 64)
+    for (int l = tid; l < nrej + 2; l += 64) {
+      if (l == 0) {
+        const float lt = Elem<DT>::at(A.tgt, (t0 + v) * (long long)A.V + x);
+        P.tm[0] = emass_t(lt, P.mt[v], c64, c32, P.tab) / P.zt[v];
+      } else {
+        const int w = l <= nrej ? P.rej[l - 1] : c;
+        const float ld = Elem<DT>::at(A.dft, (d0 + w - 1) * (long long)A.V + x);
+        P.tm[l] = emass_t(ld, P.md[w], c64, c32, P.tab) / P.zd[w];
+      }
+    }
+  __syncthreads();
+  if (tid == 0) {
+    double R = P.tm[0];
+    for (int j = 0; j < nrej; ++j)
+      if (!P.skip[j]) R = fmax(0.0, R - P.S[j] * P.tm[j + 1]);
+    P.flag = (double)A.ua[t0 + c] * P.tm[nrej + 1] * P.S[nrej] < R;
+    P.rej[nrej] = c;
+    P.skip[nrej] = 0;
+  }
+  __syncthreads();
+}
+
+// Next rejected sibling at or after k whose residual step applies (nrej if none).
+__device__ __forceinline__ int next_live(const LLSpace& P, int k, int nrej) {
+  while (k < nrej && P.skip[k]) ++k;
+  return k;
+}
+
+// Segments of the pass: 64 consecutive 16-byte vectors of a row (64 * epv
+// tokens), one vector per lane.
+template <int DT> struct Seg { static constexpr int tok = 64 * Elem<DT>::kPerVec; };
+constexpr int kSegBatch = 2;  // segments of one wave whose loads are in flight together
+
+// R at the lane's vector of up to kSegBatch segments (seg[i] < 0: none) of the
+// current node: R[i*epv + e] for token (seg[i]*64 + lane)*epv + e. The vectors
+// of one row are loaded together, and the next rejected sibling's row is in
+// flight while the current one is applied.
+template <int DT>
+__device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P, const char* trow, long long d0,
+                                              int v, int nrej, const int (&seg)[kSegBatch], int lane, double c64,
+                                              float c32, double (&R)[kSegBatch * Elem<DT>::kPerVec]) {
+  constexpr int epv = Elem<DT>::kPerVec;
+  constexpr int es = sizeof(typename Elem<DT>::T);
+  auto drow = [&](int k) {
+    return reinterpret_cast<const char*>(A.dft) + (size_t)(d0 + P.rej[k] - 1) * (size_t)A.V * es;
+  };
+  // tokens past V (and absent segments) read as -inf: zero mass
+  auto tokj = [&](int i) { return seg[i] < 0 ? A.V : (seg[i] * 64 + lane) * epv; };
+  uint4 w[kSegBatch], wn[kSegBatch];
+#pragma unroll
+  for (int i = 0; i < kSegBatch; ++i) w[i] = load_vec<DT>(trow, tokj(i), A.V);
+  int k = next_live(P, 0, nrej);
+  if (k < nrej) {
+    const char* dr = drow(k);
+#pragma unroll
+    for (int i = 0; i < kSegBatch; ++i) wn[i] = load_vec<DT>(dr, tokj(i), A.V);
+  }
+  {
+    const float mt = P.mt[v];
+    const double izt = 1.0 / P.zt[v];
+#pragma unroll
+    for (int i = 0; i < kSegBatch; ++i) {
+      float x[epv];
+      unpack<DT>(w[i], x);
+#pragma unroll
+      for (int e = 0; e < epv; ++e) R[i * epv + e] = emass_t(x[e], mt, c64, c32, P.tab) * izt;
+    }
+  }
+  while (k < nrej) {
+#pragma unroll
+    for (int i = 0; i < kSegBatch; ++i) w[i] = wn[i];
+    const int c = P.rej[k];
+    const double s = P.S[k] / P.zd[c];
+    const float md = P.md[c];
+    const int k2 = next_live(P, k + 1, nrej);
+    if (k2 < nrej) {
+      const char* dr = drow(k2);
+#pragma unroll
+      for (int i = 0; i < kSegBatch; ++i) wn[i] = load_vec<DT>(dr, tokj(i), A.V);
+    }
+#pragma unroll
+    for (int i = 0; i < kSegBatch; ++i) {
+      float x[epv];
+      unpack<DT>(w[i], x);
+#pragma unroll
+      for (int e = 0; e < epv; ++e) R[i * epv + e] = fmax(0.0, R[i * epv + e] - s * emass_t(x[e], md, c64, c32, P.tab));
+    }
+    k = k2;
+  }
+}
+
+// One pass: the team's waves take the segments in turn (wave g of the team:
+// segments g, g + nw, ...), kSegBatch at a time, and store each segment's sum
+// of R; then the team meets. Returns false when the wait ran out of polls.
+template <int DT>
+__device__ bool team_pass(const LLArgs& A, LLSpace& P, long long t0, long long d0, int v, int nrej, double* buf,
+                          int* ctr, int target, int rank, double c64, float c32) {
+  constexpr int epv = Elem<DT>::kPerVec;
+  constexpr int es = sizeof(typename Elem<DT>::T);
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int nw = A.G * kLLWaves;
+  const char* trow = reinterpret_cast<const char*>(A.tgt) + (size_t)(t0 + v) * (size_t)A.V * es;
+  for (int s0 = rank * kLLWaves + wv; s0 < A.nseg; s0 += nw * kSegBatch) {
+    int seg[kSegBatch];
+#pragma unroll
+    for (int i = 0; i < kSegBatch; ++i) seg[i] = s0 + i * nw < A.nseg ? s0 + i * nw : -1;
+    double R[kSegBatch * epv];
+    residual_segs<DT>(A, P, trow, d0, v, nrej, seg, lane, c64, c32, R);
+#pragma unroll
+    for (int i = 0; i < kSegBatch; ++i) {
+      double s = 0.0;
+#pragma unroll
+      for (int e = 0; e < epv; ++e) s += R[i * epv + e];
+      s = wave_sum(s);
+      if (lane == 0 && seg[i] >= 0)
+        __hip_atomic_store(reinterpret_cast<uint64_t*>(buf) + seg[i], f64_bits(s), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // the segment sums are complete before the count
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    atomicAdd(ctr, 1);
+    int seen = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int polls = 0;
+    while (seen < target && polls < kSpinPolls) {
+      __builtin_amdgcn_s_sleep(8);
+      seen = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ++polls;
+    }
+    __threadfence();
+    P.wait_ok = seen >= target;
+  }
+  __syncthreads();
+  return P.wait_ok != 0;
+}
+
+// Children of node v in ascending index order into P.kids / P.nk.
+__device__ __forceinline__ void list_children(LLSpace& P, int N, int v) {
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  int base = 0;
+  for (int c0 = 1; c0 < N; c0 += kLLThreads) {
+    const int c = c0 + tid;
+    const bool f = c < N && P.par[c] == v;
+    const unsigned long long m = __ballot(f);
+    if (lane == 0) P.cnt[wv] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wv; ++w) off += P.cnt[w];
+    if (f) P.kids[off + __popcll(m & ((1ull << lane) - 1ull))] = c;
+    for (int w = 0; w < kLLWaves; ++w) base += P.cnt[w];
+    __syncthreads();
+  }
+  if (tid == 0) P.nk = base;
+  __syncthreads();
+}
+
+// The inverse-CDF pick of the final token by wave 0 of the team's first
+// workgroup: the segment whose running sum first exceeds u * S, then the token
+// in it; the last token of positive mass when rounding leaves none.
+template <int DT>
+__device__ int pick_token(const LLArgs& A, LLSpace& P, long long t0, long long d0, int v, int nrej,
+                          const double* buf, double thr, double c64, float c32, int lane) {
+  constexpr int epv = Elem<DT>::kPerVec;
+  // the segment
+  double base = 0.0;
+  int sg = -1, last_pos = -1;
+  for (int k0 = 0; k0 * 64 < A.nseg && sg < 0; k0 += kSegLoads) {
+    double sv[kSegLoads];
+    load_segments(buf, A.nseg, k0, lane, sv);
+#pragma unroll
+    for (int k = 0; k < kSegLoads; ++k) {
+      if (sg >= 0) break;
+      const int t0w = (k0 + k) * 64;
+      const double s = sv[k];
+      const double incl = wave_incl_scan(s) + base;
+      const unsigned long long hit = __ballot(incl > thr && s > 0.0);
+      const unsigned long long pos = __ballot(s > 0.0);
+      if (pos) last_pos = t0w + 63 - __clzll(pos);
+      if (hit) {
+        const int l = __ffsll((long long)hit) - 1;
+        sg = t0w + l;
+        base = l > 0 ? lane_f64(incl, l - 1) : base;
+      } else {
+        base = lane_f64(incl, 63);
+      }
+    }
+  }
+  const bool fallback = sg < 0;
+  if (fallback) sg = last_pos;
+  if (sg < 0) return -1;
+  // the token inside the segment, in ascending order (lane, element)
+  constexpr int es = sizeof(typename Elem<DT>::T);
+  const char* trow = reinterpret_cast<const char*>(A.tgt) + (size_t)(t0 + v) * (size_t)A.V * es;
+  int seg[kSegBatch];
+  seg[0] = sg;
+#pragma unroll
+  for (int i = 1; i < kSegBatch; ++i) seg[i] = -1;
+  double R[kSegBatch * epv];
+  residual_segs<DT>(A, P, trow, d0, v, nrej, seg, lane, c64, c32, R);
+  const int jl = (sg * 64 + lane) * epv;
+  double s = 0.0;
+#pragma unroll
+  for (int e = 0; e < epv; ++e) s += R[e];
+  const double incl = wave_incl_scan(s) + base;
+  int mylast = -1;
+#pragma unroll
+  for (int e = 0; e < epv; ++e)
+    if (R[e] > 0.0) mylast = jl + e;
+  const int ylast = wave_minmax<true>(mylast);
+  int y = -1;
+  const unsigned long long hit = fallback ? 0ull : __ballot(incl > thr && s > 0.0);
+  if (hit) {
+    const int l = __ffsll((long long)hit) - 1;
+    const double excl = l > 0 ? lane_f64(incl, l - 1) : base;
+    int mine = -1;
+    if (lane == l) {
+      double C = excl;
+#pragma unroll
+      for (int e = 0; e < epv; ++e) {
+        C += R[e];
+        if (mine < 0 && R[e] > 0.0 && C > thr) mine = jl + e;
+      }
+    }
+    y = __builtin_amdgcn_readlane(mine, l);
+  }
+  return y >= 0 ? y : ylast;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kLLThreads) void k_tree_lossless(LLArgs A) {
+  __shared__ LLSpace P;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int team = blockIdx.x / A.G, rank = blockIdx.x - team * A.G;
+  const int N = A.N, width = A.max_depth + 1;
+  if (tid < 64) P.tab[tid] = exp2_f64((double)tid * 0.015625);
+  int passes = 0;  // passes of this team so far (the same in all its workgroups)
+  bool alive = true;
+  double* const sums = A.sums + (size_t)team * 2 * A.nseg;
+  int* const ctr = A.ctr + team;
+  for (int b = team; b < A.B; b += A.nteams) {
+    const float T = A.temperature[b];
+    const bool greedy = T == 0.0f;
+    const bool t_ok = temperature_ok(T);
+    const float c32 = (!t_ok || greedy) ? 0.0f : c32_of(T);
+    const double c64 = (!t_ok || greedy) ? 0.0 : c64_of(T);
+    const long long t0 = (long long)b * N, d0 = (long long)b * (N - 1);
+    int32_t* orow = A.out + (long long)b * width;
+    int32_t* nrow = A.out_nodes + (long long)b * width;
+    __syncthreads();
+    if (tid == 0) P.bad = (t_ok && alive) ? 0 : 1;
+    __syncthreads();
+    // --- tree, validation and the statistics of every row
+    bool lbad = false;
+    // one row per thread: target rows 0..N-1, then (sampling) draft rows of nodes 1..N-1
+    const int nrows = greedy ? N : 2 * N - 1;
+    for (int r = tid; r < nrows && t_ok; r += kLLThreads) {
+      if (r < N) {
+        const int v = r;
+        const int p = A.parents[t0 + v], x = A.tokens[t0 + v];
+        P.par[v] = p;
+        P.tok[v] = x;
+        lbad |= v == 0 ? p != -1 : (p < 0 || p >= v || x < 0 || x >= A.V);
+        const RowStat st = merge_row(A.part + (t0 + v) * A.nchunk, A.nchunk, c32, greedy);
+        lbad |= !st.ok;
+        P.mt[v] = st.m;
+        P.zt[v] = st.Z;
+        P.idx[v] = st.idx;
+        if (!greedy) lbad |= !uniform_ok(A.us[t0 + v]);
+        P.depth[0][v] = v == 0 ? 0 : (1 << 20);
+      } else {
+        const int v = r - N + 1;
+        lbad |= !uniform_ok(A.ua[t0 + v]);
+        const RowStat sd = merge_row(A.part + (A.RT + d0 + v - 1) * A.nchunk, A.nchunk, c32, false);
+        lbad |= !sd.ok;
+        P.md[v] = sd.m;
+        P.zd[v] = sd.Z;
+      }
+    }
+    if (lbad) P.bad = 1;
+    __syncthreads();
+    int cur = 0;
+    if (!P.bad) {
+      // depths by repeated relaxation (parents precede children)
+      for (int it = 0; it <= A.max_depth; ++it) {
+        for (int v = tid; v < N; v += kLLThreads)
+          P.depth[cur ^ 1][v] = v == 0 ? 0 : min(P.depth[cur][P.par[v]] + 1, 1 << 20);
+        __syncthreads();
+        cur ^= 1;
+      }
+      for (int v = tid; v < N; v += kLLThreads)
+        if (P.depth[cur][v] > A.max_depth) P.bad = 1;
+    }
+    __syncthreads();
+    if (rank == 0)
+      for (int k = tid; k < width; k += kLLThreads) {
+        orow[k] = -1;
+        nrow[k] = -1;
+      }
+    if (P.bad) {
+      if (rank == 0 && tid == 0) A.num_acc[b] = -1;
+      continue;
+    }
+    // --- greedy: follow the first child holding the argmax
+    if (greedy) {
+      if (rank != 0) continue;
+      int v = 0, d = 0;
+      for (;;) {
+        if (tid == 0) P.flag = 0x7fffffff;
+        __syncthreads();
+        for (int c = 1 + tid; c < N; c += kLLThreads)
+          if (P.par[c] == v && P.tok[c] == P.idx[v]) atomicMin(&P.flag, c);
+        __syncthreads();
+        const int c = P.flag;
+        __syncthreads();
+        if (c == 0x7fffffff) break;
+        if (tid == 0) {
+          orow[d] = P.tok[c];
+          nrow[d] = c;
+        }
+        ++d;
+        v = c;
+      }
+      if (tid == 0) {
+        orow[d] = P.idx[v];
+        A.num_acc[b] = d;
+      }
+      continue;
+    }
+    // --- sampling walk
+    int v = 0, d = 0, nrej = 0;
+    bool have_sums = false;  // the last pass's segment sums are those of the current R
+    bool failed = false;
+    for (;;) {
+      list_children(P, N, v);
+      if (tid == 0) P.S[0] = 1.0;
+      nrej = 0;
+      have_sums = false;
+      int accepted = -1;
+      for (int i = 0; i < P.nk; ++i) {
+        const int c = P.kids[i];
+        child_test<DT>(A, P, t0, d0, v, nrej, c, c64, c32);
+        if (P.flag) {
+          accepted = c;
+          break;
+        }
+        // rejected: the next residual's total
+        ++nrej;
+        ++passes;
+        if (!team_pass<DT>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr, passes * A.G, rank,
+                           c64, c32)) {
+          failed = true;
+          break;
+        }
+        if (wv == 0) {
+          const double S = sum_segments(sums + (size_t)(passes & 1) * A.nseg, A.nseg, lane);
+          if (lane == 0) {
+            if (S > 0.0) {
+              P.S[nrej] = S;
+            } else {  // underflow: keep r
+              P.skip[nrej - 1] = 1;
+              P.S[nrej] = P.S[nrej - 1];
+            }
+          }
+        }
+        __syncthreads();
+        have_sums = !P.skip[nrej - 1];
+      }
+      if (failed) break;
+      if (accepted < 0) break;
+      if (rank == 0 && tid == 0) {
+        orow[d] = P.tok[accepted];
+        nrow[d] = accepted;
+      }
+      ++d;
+      v = accepted;
+    }
+    if (!failed && !have_sums) {
+      ++passes;
+      failed = !team_pass<DT>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr, passes * A.G,
+                              rank, c64, c32);
+    }
+    if (failed) {
+      // a team wait ran out of polls: this team's remaining requests report -1
+      alive = false;
+      if (rank == 0 && tid == 0) A.num_acc[b] = -1;
+      if (rank == 0)
+        for (int k = tid; k < width; k += kLLThreads) orow[k] = -1;
+      continue;
+    }
+    if (rank == 0 && wv == 0) {
+      const double* buf = sums + (size_t)(passes & 1) * A.nseg;
+      const double S = sum_segments(buf, A.nseg, lane);
+      const double thr = (double)A.us[t0 + v] * S;
+      const int y = pick_token<DT>(A, P, t0, d0, v, nrej, buf, thr, c64, c32, lane);
+      if (lane == 0) {
+        orow[d] = y;
+        A.num_acc[b] = d;
+      }
+    }
+  }
+}
+
+int lossless_segments(int V, int dt) {
+  const int tok = 64 * (dt == 1 ? 8 : 4);
+  return (V + tok - 1) / tok;
+}
+
+hipError_t launch_tree_lossless(int dt, const void* tgt, const void* dft, int V, const Layout& L, int max_depth,
+                                const int32_t* tokens, const int32_t* parents, const float* ua, const float* us,
+                                const float* temperature, const Partial* part, int nchunk, double* sums, int* ctr,
+                                int32_t* out, int32_t* out_nodes, int32_t* num_acc, hipStream_t st) {
+  if (L.B == 0) return hipSuccess;
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
+  const void* fn = dt == 1 ? reinterpret_cast<const void*>(&k_tree_lossless<1>)
+                           : reinterpret_cast<const void*>(&k_tree_lossless<0>);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kLLThreads, 0);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  const long long resident = (long long)per_cu * cus;
+  // workgroups per request: every resident slot in use, at most 16 (a pass
+  // then has up to 64 waves), and every workgroup of the launch resident at once
+  const long long want = resident / L.B;
+  int G = (int)(want < 1 ? 1 : (want > 16 ? 16 : want));
+  if (G > resident) G = (int)resident;
+  long long nteams = resident / G;
+  if (nteams > L.B) nteams = L.B;
+  LLArgs A;
+  A.tgt = tgt;
+  A.dft = dft;
+  A.V = V;
+  A.N = L.gamma;
+  A.B = L.B;
+  A.max_depth = max_depth;
+  A.tokens = tokens;
+  A.parents = parents;
+  A.ua = ua;
+  A.us = us;
+  A.temperature = temperature;
+  A.part = part;
+  A.nchunk = nchunk;
+  A.RT = L.RT;
+  A.sums = sums;
+  A.ctr = ctr;
+  A.G = G;
+  A.nteams = (int)nteams;
+  A.nseg = lossless_segments(V, dt);
+  A.out = out;
+  A.out_nodes = out_nodes;
+  A.num_acc = num_acc;
+  void* args[] = {&A};
+  return hipLaunchCooperativeKernel(fn, dim3((unsigned)(nteams * G)), dim3(kLLThreads), args, 0, st);
+}
+
+}  // namespace sv

@@ -45,6 +45,11 @@ _lib.spec_verify_ragged.argtypes = [_P, _P, _I32, _P, _I32, _P, _P, _P, _P, _I32
 _lib.spec_verify_ragged.restype = ctypes.c_int
 _lib.spec_verify_tree.argtypes = [_P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]
 _lib.spec_verify_tree.restype = ctypes.c_int
+_lib.spec_verify_tree_lossless_workspace_bytes.argtypes = [_I32, _I32, _I32, _I32]
+_lib.spec_verify_tree_lossless_workspace_bytes.restype = _SZ
+_lib.spec_verify_tree_lossless.argtypes = [_P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P, _P,
+                                           _SZ, _P]
+_lib.spec_verify_tree_lossless.restype = ctypes.c_int
 _lib.spec_row_softmax_stats.argtypes = [_P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.spec_row_softmax_stats.restype = ctypes.c_int
 _lib.spec_sample_rows_workspace_bytes.argtypes = [_I32, _I32, _I32]
@@ -126,6 +131,10 @@ def spec_verify_tree_workspace_bytes(B, N, V, dtype) -> int:
     return _lib.spec_verify_tree_workspace_bytes(B, N, V, dtype)
 
 
+def spec_verify_tree_lossless_workspace_bytes(B, N, V, dtype) -> int:
+    return _lib.spec_verify_tree_lossless_workspace_bytes(B, N, V, dtype)
+
+
 def spec_row_softmax_stats_workspace_bytes(rows, V, dtype) -> int:
     return _lib.spec_row_softmax_stats_workspace_bytes(rows, V, dtype)
 
@@ -152,6 +161,15 @@ def spec_verify_tree(target_logits, draft_logits, dtype, node_tokens, parents, u
                                  _ptr(u_accept), _ptr(u_sample), _ptr(temperature), B, N, V, max_depth,
                                  _ptr(out_tokens), _ptr(out_nodes), _ptr(num_accepted), _ptr(workspace),
                                  workspace_bytes, stream)
+
+
+def spec_verify_tree_lossless(target_logits, draft_logits, dtype, node_tokens, parents, u_accept, u_sample,
+                              temperature, B, N, V, max_depth, out_tokens, out_nodes, num_accepted, workspace,
+                              workspace_bytes, stream) -> int:
+    return _lib.spec_verify_tree_lossless(_ptr(target_logits), _ptr(draft_logits), dtype, _ptr(node_tokens),
+                                          _ptr(parents), _ptr(u_accept), _ptr(u_sample), _ptr(temperature), B, N, V,
+                                          max_depth, _ptr(out_tokens), _ptr(out_nodes), _ptr(num_accepted),
+                                          _ptr(workspace), workspace_bytes, stream)
 
 
 def spec_row_softmax_stats(logits, dtype, rows, V, temperature, out_max, out_logz, out_argmax, workspace,
@@ -302,6 +320,24 @@ def verify_tree(target, draft, node_tokens, parents, u_accept, u_sample, tempera
     ws = workspace if workspace is not None else _ws(dev, nbytes)
     _check(spec_verify_tree(target, draft, dt, node_tokens, parents, u_accept, u_sample, temperature, B, N, V,
                             max_depth, out, nodes, na, ws, ws.numel(), _stream(dev)))
+    return out, nodes, na
+
+
+def verify_tree_lossless(target, draft, node_tokens, parents, u_accept, u_sample, temperature, max_depth, *,
+                         workspace=None):
+    """Lossless multi-candidate tree verify (siblings tried in order against the running residual).
+    target [B, N, V], draft [B, N-1, V]; returns (out_tokens, out_nodes, num_accepted)."""
+    B, N, V = target.shape
+    dt = logits_dtype(target)
+    _need(target, None, "target")
+    dev = target.device
+    out = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    nodes = torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev)
+    na = torch.empty(B, dtype=torch.int32, device=dev)
+    nbytes = spec_verify_tree_lossless_workspace_bytes(B, N, V, dt)
+    ws = workspace if workspace is not None else _ws(dev, nbytes)
+    _check(spec_verify_tree_lossless(target, draft, dt, node_tokens, parents, u_accept, u_sample, temperature, B, N,
+                                     V, max_depth, out, nodes, na, ws, ws.numel(), _stream(dev)))
     return out, nodes, na
 
 
