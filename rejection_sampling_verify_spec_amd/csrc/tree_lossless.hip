@@ -233,8 +233,9 @@ __device__ bool team_pass(const LLArgs& A, LLSpace& P, long long t0, long long d
   // the segment sums are complete before the count
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // (every value the team exchanges is a device-scope atomic access, so the
+  // completed stores need no fence: a fence would write back the whole L2)
   if (tid == 0) {
-    __threadfence();
     atomicAdd(ctr, 1);
     int seen = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int polls = 0;
@@ -243,7 +244,6 @@ __device__ bool team_pass(const LLArgs& A, LLSpace& P, long long t0, long long d
       seen = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ++polls;
     }
-    __threadfence();
     P.wait_ok = seen >= target;
   }
   __syncthreads();
