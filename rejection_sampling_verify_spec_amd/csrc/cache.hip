@@ -10,9 +10,10 @@
 // positions into the ring and moving the length back afterwards would
 // overwrite up to gamma-n live window positions once the ring has wrapped.
 //
-// One workgroup per (request, kept position, block of rows) copies rows of E
-// bytes with 16-, 4- or 1-byte accesses; the sources of one position are one
-// contiguous range, the destinations rows of E bytes at a stride of (S+W)*E.
+// One workgroup per (request, block of rows) copies the kept positions of those
+// rows with 16-, 4- or 1-byte accesses: consecutive positions sit in adjacent
+// ring slots, so each row is written as runs of (n+1)*E bytes (two runs where
+// the ring wraps) instead of single rows of E bytes at a stride of (S+W)*E.
 //
 // Draft window [Window 窗口数学; Window block table 的裁剪方式]: one wave per
 // request computes its windowed length and gathers its block-table row from
@@ -23,7 +24,7 @@ namespace svc {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;         // accesses in flight per thread and tensor
-constexpr int kBlockAccesses = 2048;  // target accesses per workgroup and tensor
+constexpr int kBlockAccesses = 512;  // accesses per workgroup and tensor, at most (measured best)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte access
 
 template <typename VT>
@@ -35,48 +36,48 @@ __global__ __launch_bounds__(kThreads) void k_kv_commit(char* __restrict__ kc, c
                                                         int S, int W, int rpb, int nchunk) {
   const long long blk = blockIdx.x;
   const int c = (int)(blk % nchunk);
-  const long long item = blk / nchunk;
-  const int j = (int)(item % (gamma + 1));
-  const long long b = item / (gamma + 1);
+  const long long b = blk / nchunk;
   const int P = len_in[b];
   const int n = nacc[b];
   const bool ok = n >= 0 && n <= gamma && P >= 0 && (long long)P + n + 1 <= 0x7fffffffLL;
-  if (j == 0 && c == 0 && threadIdx.x == 0) len_out[b] = ok ? P + n + 1 : P;
-  if (!ok || j > n) return;
-  const long long pos = (long long)P + j;
-  // a later kept position maps to the same ring slot and is the one kept
-  if (pos >= S && pos + W <= (long long)P + n) return;
+  if (c == 0 && threadIdx.x == 0) len_out[b] = ok ? P + n + 1 : P;
+  if (!ok) return;
+  // kept positions P + j0 .. P + n: a later kept position takes the ring slot of
+  // any earlier one W positions before it
+  int j0 = 0;
+  while (j0 <= n && (long long)P + j0 >= S && (long long)P + j0 + W <= (long long)P + n) ++j0;
+  const int np = n + 1 - j0;
   const long long cap = (long long)S + W;
-  const long long s = ring_slot(pos, S, W);
   const int r0 = c * rpb;
   const int nr = min(rpb, R - r0);
   const int vpr = (int)(E / (long long)sizeof(VT));
-  const int total = nr * vpr;
-  const long long src = ((b * (gamma + 1) + j) * R + r0) * E;
-  const VT* __restrict__ ks = reinterpret_cast<const VT*>(kn + src);
-  const VT* __restrict__ vs = reinterpret_cast<const VT*>(vn + src);
-  const long long dst = ((b * R + r0) * cap + s) * E;
-  char* __restrict__ kd = kc + dst;
-  char* __restrict__ vd = vc + dst;
+  const int per_row = np * vpr;
+  const int total = nr * per_row;
   const long long row_stride = cap * E;
   for (int base = threadIdx.x; base < total; base += kThreads * kUnroll) {
     VT a[kUnroll], v[kUnroll];
+    long long dst[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int i = base + u * kThreads;
       if (i < total) {
-        a[u] = ks[i];
-        v[u] = vs[i];
+        const int r = i / per_row;
+        const int rem = i - r * per_row;
+        const int jj = rem / vpr;
+        const int w = rem - jj * vpr;
+        const int j = j0 + jj;
+        const long long src = ((b * (gamma + 1) + j) * R + r0 + r) * E + (long long)w * (long long)sizeof(VT);
+        a[u] = *reinterpret_cast<const VT*>(kn + src);
+        v[u] = *reinterpret_cast<const VT*>(vn + src);
+        dst[u] = (b * R + r0 + r) * row_stride + ring_slot((long long)P + j, S, W) * E + (long long)w * (long long)sizeof(VT);
       }
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int i = base + u * kThreads;
       if (i < total) {
-        const int r = i / vpr;
-        const long long off = r * row_stride + (long long)(i - r * vpr) * (long long)sizeof(VT);
-        *reinterpret_cast<VT*>(kd + off) = a[u];
-        *reinterpret_cast<VT*>(vd + off) = v[u];
+        *reinterpret_cast<VT*>(kc + dst[u]) = a[u];
+        *reinterpret_cast<VT*>(vc + dst[u]) = v[u];
       }
     }
   }
@@ -91,10 +92,11 @@ hipError_t launch_kv_commit(char* kc, char* vc, const char* kn, const char* vn, 
   const bool a4 = E % 4 == 0 && al(kc, 4) && al(vc, 4) && al(kn, 4) && al(vn, 4);
   const int vb = a16 ? 16 : a4 ? 4 : 1;
   const long long vpr = E / vb;
-  const int rpb = (int)(vpr >= kBlockAccesses ? 1 : (kBlockAccesses / vpr < R ? kBlockAccesses / vpr : R));
+  const long long per_row_max = vpr * (gamma + 1);
+  const int rpb = (int)(per_row_max >= kBlockAccesses ? 1 : (kBlockAccesses / per_row_max < R ? kBlockAccesses / per_row_max : R));
   const int nchunk = (R + rpb - 1) / rpb;
-  const long long grid = (long long)B * (gamma + 1) * nchunk;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const long long grid = (long long)B * nchunk;
+  if (grid > 0x7fffffffLL || (long long)rpb * per_row_max > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const dim3 g((unsigned)grid), t(kThreads);
   if (vb == 16)
     hipLaunchKernelGGL(k_kv_commit<u32x4>, g, t, 0, st, kc, vc, kn, vn, len_in, nacc, len_out, gamma, R, E, S, W,
