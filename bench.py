@@ -373,6 +373,23 @@ def run_cache_bench(args):
     return 0 if parity_ok is not False else 1
 
 
+def read_ceiling(sv, tensors, reps=20):
+    """The practical read rate (GB/s) of a plain probe kernel over the given device tensors, with the
+    streaming kernel's load pattern; events on the launch stream around `reps` rounds."""
+    import torch
+    outs = [sv.read_probe(t) for t in tensors]  # warm-up, and the output buffers
+    nbytes = sum(t.numel() * t.element_size() // 16 * 16 for t in tensors)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for t, o in zip(tensors, outs):
+            sv.read_probe(t, o)
+    e1.record()
+    torch.cuda.synchronize()
+    return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
 def run_bench(args):
     import numpy as np
     import torch
@@ -420,6 +437,9 @@ def run_bench(args):
         walk_ms, k1_ms = k1_ms[1::2], k1_ms[0::2]
     k1_avg_ms = float(np.mean(k1_ms)) if k1_ms else float("nan")
     k1_gbps = k1_bytes / (k1_avg_ms * 1e-3) / 1e9
+
+    ceiling = read_ceiling(sv, [copies[0]["logits"]] if name == "sample" else
+                           [copies[0]["target"], copies[0]["draft"]])
 
     # CPU oracle on the host cores: whole verify steps of the same batch, repeated until about
     # args.cpu_seconds of wall time have passed (at least one step)
@@ -490,6 +510,9 @@ def run_bench(args):
                       f"fp64 oracle, {cores} threads, {cpu_s:.2f} s wall",
         },
         "parity_vs_oracle": parity_ok,
+        "read_ceiling": {"kernel": "k_read_probe", "gbps": round(ceiling, 1),
+                         "frac_of_peak": round(ceiling / HBM_PEAK_GBPS, 4),
+                         "row_stats_frac_of_ceiling": round(k1_gbps / ceiling, 4)},
     }
     if not sample:
         line["mean_num_accepted"] = round(float(np.mean(na[na >= 0])), 4)

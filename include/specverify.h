@@ -329,6 +329,17 @@ int spec_draft_window(const int32_t* seq_lens, int32_t B, int32_t window, int32_
 int spec_draft_window_host(const int32_t* seq_lens, int32_t n, int32_t window, int32_t block_size,
                            int32_t future_offset, int32_t* windowed_lens);
 
+/*
+ * Measurement aid, not a step of the method: reads `bytes` at `src` (device,
+ * 16-byte aligned, a multiple of 16) with the load pattern of the streaming
+ * statistics kernel and writes one folded word per wave to `out` (device,
+ * spec_read_probe_words(bytes) words), so that the read rate this part
+ * reaches in practice can be reported next to the HBM peak. Asynchronous on
+ * `stream`; SV_EINVAL, SV_EALIGN or SV_EHIP.
+ */
+size_t spec_read_probe_words(size_t bytes);
+int spec_read_probe(const void* src, size_t bytes, uint32_t* out, void* stream);
+
 /* Human-readable text for an sv_status. */
 const char* spec_verify_strerror(int status);
 

@@ -4,7 +4,8 @@ The verify path lives in ``libspecverify.so`` (HIP kernels for gfx950 behind
 the C ABI in ``include/specverify.h``); ``specverify`` is its ctypes binding.
 """
 from .specverify import (  # noqa: F401
-    SV_BF16, SV_F32, SpecVerifyError, Workspace, draft_window, kv_commit, kv_valid_slots, row_softmax_stats,
+    SV_BF16, SV_F32, SpecVerifyError, Workspace, draft_window, kv_commit, kv_valid_slots, read_probe,
+    row_softmax_stats, spec_read_probe, spec_read_probe_words,
     sample_rows, spec_draft_window, spec_draft_window_host, spec_draft_window_max_blocks, spec_kv_commit,
     spec_kv_valid_slots, spec_row_softmax_stats,
     spec_sample_rows, spec_sample_rows_workspace_bytes,

@@ -22,6 +22,10 @@ hipError_t launch_tree_lossless(int dt, const void* tgt, const void* dft, int V,
                                 int32_t* out, int32_t* out_nodes, int32_t* num_acc, hipStream_t st);
 int lossless_segments(int V, int dt);
 }  // namespace sv
+namespace svp {
+long long probe_blocks(long long nvec);
+hipError_t launch_read_probe(const void* src, long long nvec, uint32_t* out, hipStream_t st);
+}  // namespace svp
 
 static_assert(sizeof(Partial) == 8, "Partial layout");
 static_assert(sizeof(TileRec) == 128, "TileRec layout");
@@ -408,6 +412,17 @@ int spec_draft_window_host(const int32_t* seq_lens, int32_t n, int32_t window, i
   if (n > 0 && (!seq_lens || !windowed_lens)) return SV_EINVAL;
   for (int32_t i = 0; i < n; ++i) windowed_lens[i] = svc::window_len(seq_lens[i], window, block_size, future_offset);
   return SV_OK;
+}
+
+size_t spec_read_probe_words(size_t bytes) { return (size_t)svp::probe_blocks((long long)(bytes / 16)) * 4; }
+
+int spec_read_probe(const void* src, size_t bytes, uint32_t* out, void* stream) {
+  if (bytes == 0) return SV_OK;
+  if (!src || !out || bytes % 16 != 0 || bytes > ((size_t)1 << 46)) return SV_EINVAL;
+  if (!aligned(src, 16)) return SV_EALIGN;
+  return svp::launch_read_probe(src, (long long)(bytes / 16), out, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? SV_OK
+             : SV_EHIP;
 }
 
 const char* spec_verify_strerror(int status) {

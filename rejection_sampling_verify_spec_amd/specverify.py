@@ -67,6 +67,10 @@ _lib.spec_draft_window.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _I32, _P, _P,
 _lib.spec_draft_window.restype = ctypes.c_int
 _lib.spec_draft_window_host.argtypes = [_P, _I32, _I32, _I32, _I32, _P]
 _lib.spec_draft_window_host.restype = ctypes.c_int
+_lib.spec_read_probe_words.argtypes = [_SZ]
+_lib.spec_read_probe_words.restype = _SZ
+_lib.spec_read_probe.argtypes = [_P, _SZ, _P, _P]
+_lib.spec_read_probe.restype = ctypes.c_int
 _lib.spec_verify_strerror.argtypes = [ctypes.c_int]
 _lib.spec_verify_strerror.restype = ctypes.c_char_p
 _lib.spec_verify_version.restype = ctypes.c_int
@@ -185,6 +189,23 @@ def spec_sample_rows_workspace_bytes(rows, V, dtype) -> int:
 def spec_sample_rows(logits, dtype, rows, V, temperature, u, out_tokens, workspace, workspace_bytes, stream) -> int:
     return _lib.spec_sample_rows(_ptr(logits), dtype, rows, V, _ptr(temperature), _ptr(u), _ptr(out_tokens),
                                  _ptr(workspace), workspace_bytes, stream)
+
+
+def spec_read_probe_words(nbytes) -> int:
+    return _lib.spec_read_probe_words(nbytes)
+
+
+def spec_read_probe(src, nbytes, out, stream) -> int:
+    return _lib.spec_read_probe(_ptr(src), nbytes, _ptr(out), stream)
+
+
+def read_probe(t, out=None):
+    """Read every byte of device tensor t with the streaming kernel's load pattern (a measurement aid)."""
+    nbytes = t.numel() * t.element_size() // 16 * 16
+    if out is None:
+        out = torch.empty(max(spec_read_probe_words(nbytes), 1), dtype=torch.int32, device=t.device)
+    _check(spec_read_probe(t, nbytes, out, _stream(t.device)))
+    return out
 
 
 def spec_kv_commit(k_cache, v_cache, k_new, v_new, lengths, num_accepted, new_lengths, B, gamma, rows, row_bytes,
