@@ -151,3 +151,13 @@ def test_draft_window_host_matches_oracle():
         assert seq.tolist() == ref
     assert b.spec_draft_window_host(None, 0, 64, 16, 3, None) == b.SV_OK
     assert b.spec_draft_window_host(None, 3, 64, 16, 3, None) == b.SV_EINVAL
+
+
+def test_read_probe_rejects_bad_arguments():
+    import rejection_sampling_verify_spec_amd.specverify as b
+    assert b.spec_read_probe_words(0) == 0 and b.spec_read_probe_words(16) == 4
+    assert b.spec_read_probe_words(2048 * 16 + 16) == 8
+    assert b.spec_read_probe(256, 24, 512, None) == b.SV_EINVAL   # not a multiple of 16
+    assert b.spec_read_probe(None, 32, 512, None) == b.SV_EINVAL
+    assert b.spec_read_probe(264, 32, 512, None) == b.SV_EALIGN
+    assert b.spec_read_probe(None, 0, None, None) == b.SV_OK
