@@ -55,16 +55,19 @@ struct LLArgs {
   int32_t* num_acc;
 };
 
+// Shared memory of a workgroup (about 50 KB, so that three workgroups share a CU).
 struct LLSpace {
-  int par[kLLMaxNodes], tok[kLLMaxNodes], idx[kLLMaxNodes];
-  int depth[2][kLLMaxNodes];
-  float mt[kLLMaxNodes], md[kLLMaxNodes];
+  int par[kLLMaxNodes], tok[kLLMaxNodes];
+  float mt[kLLMaxNodes];
+  union {
+    float md[kLLMaxNodes];  // sampling: draft-row maxima
+    int idx[kLLMaxNodes];   // greedy: target-row argmax
+  };
   double zt[kLLMaxNodes], zd[kLLMaxNodes];
-  int kids[kLLMaxNodes];  // children of the current node, ascending
-  int rej[kLLMaxNodes];   // its rejected children, in order
-  int skip[kLLMaxNodes];  // 1 when that rejection's residual sum underflowed (r kept)
+  int kids[kLLMaxNodes];  // children of the current node, ascending (depths while the tree is checked)
+  int rej[kLLMaxNodes];   // its rejected children, in order (depths while the tree is checked)
+  unsigned char skip[kLLMaxNodes];  // 1 when that rejection's residual sum underflowed (r kept)
   double S[kLLMaxNodes + 1];
-  double tm[kLLMaxNodes + 1];  // masses at the token under test: target row, rejected siblings, the child
   double tab[64];
   int cnt[kLLWaves];
   int bad, flag, nk, wait_ok;
@@ -103,32 +106,41 @@ __device__ __forceinline__ double sum_segments(const double* buf, int nseg, int 
 
 // The acceptance test of child c of node v after nrej rejected siblings: wave 0
 // loads the token's logit in the target row, in each rejected sibling's draft
-// row and in c's draft row at once and forms their probabilities; thread 0
-// then applies the residual steps in order and compares (result in P.flag).
+// row and in c's draft row at once (64 at a time) and forms their
+// probabilities; the residual steps are then applied in order across the
+// lanes (result in P.flag).
 template <int DT>
 __device__ __forceinline__ void child_test(const LLArgs& A, LLSpace& P, long long t0, long long d0, int v, int nrej,
                                            int c, double c64, float c32) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int x = P.tok[c];
-  if (tid < 64)
-    for (int l = tid; l < nrej + 2; l += 64) {
+  if (tid < 64) {
+    double R = 0.0, q = 0.0;
+    for (int l0 = 0; l0 < nrej + 2; l0 += 64) {
+      const int l = l0 + lane;
+      double m = 0.0;
       if (l == 0) {
         const float lt = Elem<DT>::at(A.tgt, (t0 + v) * (long long)A.V + x);
-        P.tm[0] = emass_t(lt, P.mt[v], c64, c32, P.tab) / P.zt[v];
-      } else {
+        m = emass_t(lt, P.mt[v], c64, c32, P.tab) / P.zt[v];
+      } else if (l < nrej + 2) {
         const int w = l <= nrej ? P.rej[l - 1] : c;
         const float ld = Elem<DT>::at(A.dft, (d0 + w - 1) * (long long)A.V + x);
-        P.tm[l] = emass_t(ld, P.md[w], c64, c32, P.tab) / P.zd[w];
+        m = emass_t(ld, P.md[w], c64, c32, P.tab) / P.zd[w];
+      }
+      const int n = min(64, nrej + 2 - l0);
+      for (int k = 0; k < n; ++k) {
+        const double mk = lane_f64(m, k);
+        const int idx = l0 + k;
+        if (idx == 0) R = mk;
+        else if (idx <= nrej) R = P.skip[idx - 1] ? R : fmax(0.0, R - P.S[idx - 1] * mk);
+        else q = mk;
       }
     }
-  __syncthreads();
-  if (tid == 0) {
-    double R = P.tm[0];
-    for (int j = 0; j < nrej; ++j)
-      if (!P.skip[j]) R = fmax(0.0, R - P.S[j] * P.tm[j + 1]);
-    P.flag = (double)A.ua[t0 + c] * P.tm[nrej + 1] * P.S[nrej] < R;
-    P.rej[nrej] = c;
-    P.skip[nrej] = 0;
+    if (tid == 0) {
+      P.flag = (double)A.ua[t0 + c] * q * P.S[nrej] < R;
+      P.rej[nrej] = c;
+      P.skip[nrej] = 0;
+    }
   }
   __syncthreads();
 }
@@ -343,7 +355,7 @@ __device__ int pick_token(const LLArgs& A, LLSpace& P, long long t0, long long d
 }
 
 template <int DT>
-__global__ __launch_bounds__(kLLThreads) void k_tree_lossless(LLArgs A) {
+__global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_tree_lossless(LLArgs A) {
   __shared__ LLSpace P;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int team = blockIdx.x / A.G, rank = blockIdx.x - team * A.G;
@@ -380,9 +392,9 @@ __global__ __launch_bounds__(kLLThreads) void k_tree_lossless(LLArgs A) {
         lbad |= !st.ok;
         P.mt[v] = st.m;
         P.zt[v] = st.Z;
-        P.idx[v] = st.idx;
-        if (!greedy) lbad |= !uniform_ok(A.us[t0 + v]);
-        P.depth[0][v] = v == 0 ? 0 : (1 << 20);
+        if (greedy) P.idx[v] = st.idx;
+        else lbad |= !uniform_ok(A.us[t0 + v]);
+        P.kids[v] = v == 0 ? 0 : (1 << 20);  // depth
       } else {
         const int v = r - N + 1;
         lbad |= !uniform_ok(A.ua[t0 + v]);
@@ -394,17 +406,19 @@ __global__ __launch_bounds__(kLLThreads) void k_tree_lossless(LLArgs A) {
     }
     if (lbad) P.bad = 1;
     __syncthreads();
-    int cur = 0;
     if (!P.bad) {
-      // depths by repeated relaxation (parents precede children)
+      // depths by repeated relaxation (parents precede children), in kids / rej
+      int* dcur = P.kids;
+      int* dnext = P.rej;
       for (int it = 0; it <= A.max_depth; ++it) {
-        for (int v = tid; v < N; v += kLLThreads)
-          P.depth[cur ^ 1][v] = v == 0 ? 0 : min(P.depth[cur][P.par[v]] + 1, 1 << 20);
+        for (int v = tid; v < N; v += kLLThreads) dnext[v] = v == 0 ? 0 : min(dcur[P.par[v]] + 1, 1 << 20);
         __syncthreads();
-        cur ^= 1;
+        int* t = dcur;
+        dcur = dnext;
+        dnext = t;
       }
       for (int v = tid; v < N; v += kLLThreads)
-        if (P.depth[cur][v] > A.max_depth) P.bad = 1;
+        if (dcur[v] > A.max_depth) P.bad = 1;
     }
     __syncthreads();
     if (rank == 0)
@@ -535,10 +549,10 @@ hipError_t launch_tree_lossless(int dt, const void* tgt, const void* dft, int V,
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   const long long resident = (long long)per_cu * cus;
-  // workgroups per request: every resident slot in use, at most 16 (a pass
-  // then has up to 64 waves), and every workgroup of the launch resident at once
+  // workgroups per request: every resident slot in use, at most 32 (a pass
+  // then has up to 128 waves), and every workgroup of the launch resident at once
   const long long want = resident / L.B;
-  int G = (int)(want < 1 ? 1 : (want > 16 ? 16 : want));
+  int G = (int)(want < 1 ? 1 : (want > 32 ? 32 : want));
   if (G > resident) G = (int)resident;
   long long nteams = resident / G;
   if (nteams > L.B) nteams = L.B;
