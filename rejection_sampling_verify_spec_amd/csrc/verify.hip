@@ -123,9 +123,11 @@ hipError_t launch_verify_chain(int dt, const void* tgt, const void* dft, int V, 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
   const int cus = device_cus(dev);
-  // workgroups per request: enough for about four per CU, at most 8
+  // workgroups per request: enough for about four per CU, and 4 to 8 (large
+  // batches queue their workgroups: four per request balance dense rows better
+  // than one, measured on 1024 requests over 151,936 tokens)
   const long long want = (4ll * cus + L.B - 1) / L.B;
-  int G = (int)(want < 1 ? 1 : (want > 8 ? 8 : want));
+  int G = (int)(want < 4 ? 4 : (want > 8 ? 8 : want));
   G = env_int("SPECVERIFY_REQUEST_GROUPS", G, 1, 64);
   if ((long long)L.B * G > 0x7fffffffLL) G = 1;
   RequestArgs R;
