@@ -7,6 +7,8 @@
 // residual; 考点4 bonus].
 #include "tail.h"
 
+#include <stdlib.h>
+
 namespace sv {
 
 constexpr int kNW = 4;  // waves per workgroup
@@ -113,9 +115,14 @@ hipError_t launch_finish_jobs(int dt, const void* tgt, const void* dft, int V, i
                               TileRec* recs, const Partial* part, int nchunk, long long RT, int* done, int32_t* out,
                               int out_width, int force_exact, hipStream_t st) {
   if (B == 0) return hipSuccess;
-  // workgroups per job: enough for about four per CU, at most 8
+  // workgroups per job: enough for about four per CU, and 2 to 8 (two per job
+  // balance 1280 sampled rows better than one; SPECVERIFY_JOB_GROUPS overrides)
   const long long want = (4ll * device_cus_finish() + B - 1) / B;
-  int G = (int)(want < 1 ? 1 : (want > 8 ? 8 : want));
+  int G = (int)(want < 2 ? 2 : (want > 8 ? 8 : want));
+  if (const char* e = getenv("SPECVERIFY_JOB_GROUPS")) {
+    const int g = atoi(e);
+    if (g >= 1 && g <= 64) G = g;
+  }
   if ((long long)B * G > 0x7fffffffLL) G = 1;
   const DrawArgs A{tgt, dft, V, G, jobs, recs, part, nchunk, RT, done, out, out_width, force_exact};
   const dim3 grid((unsigned)((long long)B * G)), blk(kNW * 64);
