@@ -27,8 +27,8 @@ __global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
   const int b = blockIdx.x, v = threadIdx.x;
   const int width = max_depth + 1;
   __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_depth[2][kMaxNodes], s_ok[2][kMaxNodes];
-  __shared__ float s_mt[kMaxNodes];
-  __shared__ double s_zt[kMaxNodes];
+  __shared__ float s_mt[kMaxNodes], s_md[kMaxNodes];
+  __shared__ double s_zt[kMaxNodes], s_zd[kMaxNodes];
   __shared__ int s_idx[kMaxNodes];
   __shared__ int s_bad;
   __shared__ unsigned long long s_best;
@@ -44,6 +44,7 @@ __global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
 
   bool lbad = false;
   RowStat sd{0.f, 0.0, -1, true};
+  float lt = 0.f, ld = 0.f;  // the node's logit in its parent's target row and in its draft row
   if (v < N && t_ok) {
     const int p = parents[t0 + v];
     const int x = tokens[t0 + v];
@@ -51,7 +52,14 @@ __global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
     s_tok[v] = x;
     if (v == 0) lbad |= p != -1;
     else lbad |= p < 0 || p >= v || x < 0 || x >= V;
-    RowStat st = merge_row(part + (t0 + v) * nchunk, nchunk, c32, greedy);
+    // the logits at x load while the partials are merged
+    if (!greedy && v >= 1 && p >= 0 && p < v && x >= 0 && x < V) {
+      lt = Elem<DT>::at(tgt, (t0 + p) * (long long)V + x);
+      ld = Elem<DT>::at(dft, (d0 + v - 1) * (long long)V + x);
+    }
+    RowStat st;
+    merge_rows2(part + (t0 + v) * nchunk, greedy, part + (L.RT + d0 + v - 1) * nchunk, !greedy && v >= 1, nchunk,
+                c32, st, sd);
     lbad |= !st.ok;
     s_mt[v] = st.m;
     s_zt[v] = st.Z;
@@ -60,8 +68,9 @@ __global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
       lbad |= !uniform_ok(us[t0 + v]);
       if (v >= 1) {
         lbad |= !uniform_ok(ua[t0 + v]);
-        sd = merge_row(part + (L.RT + d0 + v - 1) * nchunk, nchunk, c32, false);
         lbad |= !sd.ok;
+        s_md[v] = sd.m;
+        s_zd[v] = sd.Z;
       }
     }
     s_depth[0][v] = v == 0 ? 0 : (1 << 20);
@@ -97,9 +106,8 @@ __global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
     if (greedy) {
       acc = x == s_idx[p];
     } else {
-      RowStat stp{s_mt[p], s_zt[p], -1, true};
-      double pt = prob_at<DT>(tgt, t0 + p, V, x, stp, c32);
-      double pd = prob_at<DT>(dft, d0 + v - 1, V, x, sd, c32);
+      const double pt = exp2_f64(((double)lt - (double)s_mt[p]) * (double)c32) / s_zt[p];
+      const double pd = exp2_f64(((double)ld - (double)sd.m) * (double)c32) / sd.Z;
       acc = (double)ua[t0 + v] * pd < pt;
     }
   }
@@ -156,9 +164,8 @@ __global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
       } else {
         J.kind = JOB_RESIDUAL;
         J.drow = d0 + c - 1;
-        RowStat sc = merge_row(part + (L.RT + d0 + c - 1) * nchunk, nchunk, c32, false);
-        J.md = sc.m;
-        J.rho = s_zt[e] / sc.Z;
+        J.md = s_md[c];
+        J.rho = s_zt[e] / s_zd[c];
       }
     }
     jobs[b] = J;

@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
         P.par[v] = p;
         P.tok[v] = x;
         lbad |= v == 0 ? p != -1 : (p < 0 || p >= v || x < 0 || x >= A.V);
-        const RowStat st = merge_row(A.part + (t0 + v) * A.nchunk, A.nchunk, c32, greedy);
+        const RowStat st = merge_row<4>(A.part + (t0 + v) * A.nchunk, A.nchunk, c32, greedy);
         lbad |= !st.ok;
         P.mt[v] = st.m;
         P.zt[v] = st.Z;
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
       } else {
         const int v = r - N + 1;
         lbad |= !uniform_ok(A.ua[t0 + v]);
-        const RowStat sd = merge_row(A.part + (A.RT + d0 + v - 1) * A.nchunk, A.nchunk, c32, false);
+        const RowStat sd = merge_row<4>(A.part + (A.RT + d0 + v - 1) * A.nchunk, A.nchunk, c32, false);
         lbad |= !sd.ok;
         P.md[v] = sd.m;
         P.zd[v] = sd.Z;
