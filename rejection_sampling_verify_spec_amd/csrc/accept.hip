@@ -25,20 +25,29 @@ __global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
     SampleJob* __restrict__ jobs) {
   const int N = L.gamma;
   const int b = blockIdx.x, v = threadIdx.x;
+  const long long t0 = (long long)b * N, d0 = (long long)b * (N - 1);
   const int width = max_depth + 1;
   __shared__ int s_par[kMaxNodes], s_tok[kMaxNodes], s_depth[2][kMaxNodes], s_ok[2][kMaxNodes];
-  __shared__ float s_mt[kMaxNodes], s_md[kMaxNodes];
+  __shared__ float s_mt[kMaxNodes], s_md[kMaxNodes], s_us[kMaxNodes];
   __shared__ double s_zt[kMaxNodes], s_zd[kMaxNodes];
   __shared__ int s_idx[kMaxNodes];
   __shared__ int s_bad;
   __shared__ unsigned long long s_best;
   __shared__ int s_child;
 
+  // the per-node inputs load in one round with the temperature
   const float T = temperature[b];
+  int p = -1, x = -1;
+  float uav = 0.f, usv = 0.f;
+  if (v < N) {
+    p = parents[t0 + v];
+    x = tokens[t0 + v];
+    usv = us[t0 + v];
+    if (v >= 1) uav = ua[t0 + v];
+  }
   const bool greedy = T == 0.0f;
   const bool t_ok = temperature_ok(T);
   const float c32 = (!t_ok || greedy) ? 0.0f : c32_of(T);
-  const long long t0 = (long long)b * N, d0 = (long long)b * (N - 1);
   if (v == 0) { s_bad = t_ok ? 0 : 1; s_best = 0ull; s_child = 0x7fffffff; }
   __syncthreads();
 
@@ -46,8 +55,6 @@ __global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
   RowStat sd{0.f, 0.0, -1, true};
   float lt = 0.f, ld = 0.f;  // the node's logit in its parent's target row and in its draft row
   if (v < N && t_ok) {
-    const int p = parents[t0 + v];
-    const int x = tokens[t0 + v];
     s_par[v] = p;
     s_tok[v] = x;
     if (v == 0) lbad |= p != -1;
@@ -65,9 +72,10 @@ __global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
     s_zt[v] = st.Z;
     s_idx[v] = st.idx;
     if (!greedy) {
-      lbad |= !uniform_ok(us[t0 + v]);
+      lbad |= !uniform_ok(usv);
+      s_us[v] = usv;
       if (v >= 1) {
-        lbad |= !uniform_ok(ua[t0 + v]);
+        lbad |= !uniform_ok(uav);
         lbad |= !sd.ok;
         s_md[v] = sd.m;
         s_zd[v] = sd.Z;
@@ -102,13 +110,12 @@ __global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
   // acceptance per node against the parent's target row
   int acc = 0;
   if (v >= 1 && v < N) {
-    const int p = s_par[v], x = s_tok[v];
     if (greedy) {
       acc = x == s_idx[p];
     } else {
       const double pt = exp2_f64(((double)lt - (double)s_mt[p]) * (double)c32) / s_zt[p];
       const double pd = exp2_f64(((double)ld - (double)sd.m) * (double)c32) / sd.Z;
-      acc = (double)ua[t0 + v] * pd < pt;
+      acc = (double)uav * pd < pt;
     }
   }
   int oc = 0;
@@ -157,7 +164,7 @@ __global__ __launch_bounds__(kMaxNodes) void k_accept_tree(
       J.u = 0.0f;
     } else {
       J.c64 = c64_of(T);
-      J.u = us[t0 + e];
+      J.u = s_us[e];
       const int c = s_child;
       if (c == 0x7fffffff) {
         J.kind = JOB_BONUS;
