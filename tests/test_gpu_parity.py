@@ -75,6 +75,29 @@ def test_chain_edge_shapes(sv):
             check_chain(sv, d, f"B={B} g={g} V={V} {dtype}")
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 600_001), ("f32", 300_007)])
+def test_chain_rows_of_many_tiles(sv, dtype, V):
+    """Rows of more than 256 sampling tiles, where the pick reads the tile records from memory instead
+    of staging them in LDS: residual and bonus draws, every fifth request greedy."""
+    d = inputgen.chain_inputs(16, 3, V, seed=V % 1000, dtype=dtype, scale=2.5, noise_sd=0.8,
+                              temperature=np.linspace(0.5, 1.5, 16))
+    d["temperature"][::5] = 0.0
+    _, na, _, _ = check_chain(sv, d, f"{dtype} V={V}")
+    assert ((na >= 0) & (na < 3)).any() and (na == 3).any()  # residual and bonus draws both happen
+
+
+def test_chain_beyond_2_31_logits(sv):
+    """One call over more than 2^31 target logits: B=112, gamma=0, V=20,000,003 bf16 (2.24e9 logits,
+    4.5 GB; the last rows lie wholly past logit 2^31 and byte 2^32), with V above 2^24, so row offsets
+    need 64-bit arithmetic and in-row indices exact integer arithmetic. Odd requests are greedy
+    (argmax), even ones draw the bonus token; several drawn tokens lie above 2^24."""
+    B, V = 112, 20_000_003
+    d = inputgen.chain_inputs(B, 0, V, seed=4343, dtype="bf16", scale=2.5, noise_sd=0.8,
+                              temperature=np.tile(np.float32([1.0, 0.0]), B // 2))
+    out, na, ref, _ = check_chain(sv, d, "2^31+ logits")
+    assert (na == 0).all() and (out[:, 0] >= 2 ** 24).sum() >= 1
+
+
 def test_temperature_extremes(sv):
     d = inputgen.chain_inputs(32, 3, 3000, seed=7, dtype="f32", scale=3.0, noise_sd=0.5,
                               temperature=np.geomspace(1e-30, 1e6, 32))

@@ -72,9 +72,11 @@ def test_sampler_mixed_temperatures(sv):
 
 
 @pytest.mark.parametrize("dtype,V", [("f32", 1), ("bf16", 1), ("f32", 7), ("bf16", 7), ("f32", 2049),
-                                     ("bf16", 4097), ("f32", 20001), ("bf16", 131075)])
+                                     ("bf16", 4097), ("f32", 20001), ("bf16", 131075), ("f32", 300007),
+                                     ("bf16", 600001)])
 def test_sampler_shapes(sv, dtype, V):
-    """Ragged vocabulary tails; odd bf16 V leaves rows off the 16-byte grid."""
+    """Ragged vocabulary tails; odd bf16 V leaves rows off the 16-byte grid; the two largest rows
+    hold more than 256 sampling tiles (the pick reads the tile records from memory)."""
     n = 37
     rows = inputgen.logit_rows(34 + V, V, np.arange(n, dtype=np.int64), scale=2.0, dtype=dtype)
     check(sv, rows, 1.0, inputgen.uniform24(34, inputgen.S_USAMP, n), f"{dtype}-V{V}")
