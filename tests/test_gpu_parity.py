@@ -320,6 +320,8 @@ def test_tree_variants(sv):
     _tree_check(sv, d, "tree root only")
     d = inputgen.tree_inputs(8, 2000, seed=44, n_nodes=200, fanout=(5, 5, 7), dtype="bf16", noise_sd=2.0)
     _tree_check(sv, d, "tree 200 nodes")
+    d = inputgen.tree_inputs(8, 600_001, seed=80, n_nodes=21, fanout=(4, 4, 1), dtype="bf16", noise_sd=1.5)
+    _tree_check(sv, d, "tree V=600001 (more than 256 sampling tiles per row)")
     bad = inputgen.tree_inputs(6, 100, seed=45, n_nodes=10, fanout=(3, 2, 1), dtype="f32")
     bad["parents"] = bad["parents"].copy()
     bad["parents"][2, 5] = 7

@@ -62,6 +62,8 @@ def test_tree_variants(sv):
            "200 nodes, ragged V")
     _check(sv, inputgen.tree_inputs(4, 2049, seed=76, n_nodes=1024, fanout=(1023,), dtype="bf16", noise_sd=3.0),
            "1023 siblings")
+    _check(sv, inputgen.tree_inputs(8, 600_001, seed=80, n_nodes=21, fanout=(4, 4, 1), dtype="bf16", noise_sd=1.5),
+           "V=600001")
     bad = inputgen.tree_inputs(6, 100, seed=77, n_nodes=10, fanout=(3, 2, 1), dtype="f32")
     bad["parents"] = bad["parents"].copy()
     bad["parents"][2, 5] = 7
