@@ -30,7 +30,7 @@
 
 namespace sv {
 
-constexpr int kLLWaves = 4;
+constexpr int kLLWaves = 12;  // three per SIMD: one workgroup fills a CU, so a team meets with few members
 constexpr int kLLThreads = kLLWaves * 64;
 constexpr int kLLMaxNodes = SV_MAX_TREE_NODES;
 constexpr int kSpinPolls = 1 << 24;  // bound of one team wait (a few seconds of polls)
@@ -55,7 +55,7 @@ struct LLArgs {
   int32_t* num_acc;
 };
 
-// Shared memory of a workgroup (about 50 KB, so that three workgroups share a CU).
+// Shared memory of a workgroup (about 50 KB; one workgroup per CU).
 struct LLSpace {
   int par[kLLMaxNodes], tok[kLLMaxNodes];
   float mt[kLLMaxNodes];
