@@ -232,13 +232,13 @@ __device__ __forceinline__ void write_skipped_rec(TileRec* rec, bool head, doubl
 // ---------------------------------------------------------------------------
 // Token masses of the draw.
 
-// 2^a in double precision for a <= 0 (NaN propagates), with tab[j] = 2^{j/64}:
+// 2^a in double precision for -1100 <= a <= 0 (the caller keeps a in range;
+// NaN propagates through the arithmetic), with tab[j] = 2^{j/64}:
 // a = n + j/64 + r with n an integer, 0 <= j < 64 and |r| <= 1/128 (r is exact:
 // a and k/64 are within a factor of two of each other or r is the tiny rest),
 // and 2^r = exp(r ln 2) by its Taylor series to degree 5 (truncation below
 // 4e-17 relative). About 3 ulp in all.
 __device__ __forceinline__ double exp2_tab(double a, const double* tab) {
-  if (!(a >= -1100.0)) return (a != a) ? a : 0.0;
   const double k = __builtin_rint(a * 64.0);
   const double r = __builtin_fma(k, -0.015625, a);
   const int ki = (int)k;
@@ -259,7 +259,8 @@ __device__ __forceinline__ double exp2_tab(double a, const double* tab) {
 // these terms enter.
 __device__ __forceinline__ double emass_t(float l, float m, double c64, float c32, const double* tab) {
   const float a32 = (l - m) * c32;
-  if (a32 < kTinyExp) return (double)exp2_f32(a32);
+  if (a32 < kTinyExp) return (double)exp2_f32(a32);  // also l = -inf
+  // here a >= kTinyExp less a relative 1e-6: inside exp2_tab's range
   return exp2_tab(((double)l - (double)m) * c64, tab);
 }
 
