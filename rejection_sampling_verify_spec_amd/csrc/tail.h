@@ -238,15 +238,24 @@ __device__ __forceinline__ void write_skipped_rec(TileRec* rec, bool head, doubl
 // a and k/64 are within a factor of two of each other or r is the tiny rest),
 // and 2^r = exp(r ln 2) by its Taylor series to degree 5 (truncation below
 // 4e-17 relative). About 3 ulp in all.
+// p * r + c as the three-operand v_fma_f64: the compiler otherwise picks the
+// accumulating form, which overwrites its addend and so copies the constant
+// coefficient into a fresh register before every step.
+__device__ __forceinline__ double fma3_f64(double p, double r, double c) {
+  double d;
+  __asm__("v_fma_f64 %0, %1, %2, %3" : "=v"(d) : "v"(p), "v"(r), "v"(c));
+  return d;
+}
+
 __device__ __forceinline__ double exp2_tab(double a, const double* tab) {
   const double k = __builtin_rint(a * 64.0);
   const double r = __builtin_fma(k, -0.015625, a);
   const int ki = (int)k;
   double p = 0x1.5d87fe78a6731p-10;  // ln2^5 / 5!
-  p = __builtin_fma(p, r, 0x1.3b2ab6fba4e77p-7);  // ln2^4 / 4!
-  p = __builtin_fma(p, r, 0x1.c6b08d704a0c0p-5);  // ln2^3 / 3!
-  p = __builtin_fma(p, r, 0x1.ebfbdff82c58fp-3);  // ln2^2 / 2!
-  p = __builtin_fma(p, r, 0x1.62e42fefa39efp-1);  // ln2
+  p = fma3_f64(p, r, 0x1.3b2ab6fba4e77p-7);  // ln2^4 / 4!
+  p = fma3_f64(p, r, 0x1.c6b08d704a0c0p-5);  // ln2^3 / 3!
+  p = fma3_f64(p, r, 0x1.ebfbdff82c58fp-3);  // ln2^2 / 2!
+  p = fma3_f64(p, r, 0x1.62e42fefa39efp-1);  // ln2
   p = __builtin_fma(p, r, 1.0);
   return __builtin_ldexp(tab[ki & 63] * p, ki >> 6);
 }
