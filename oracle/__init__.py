@@ -46,11 +46,11 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         I = ctypes.c_int
-        lib.oracle_verify_chain.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, P, P, P, P, P, P, I, I]
+        lib.oracle_verify_chain.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, P, P, P, P, P, P, P, I, I]
         lib.oracle_verify_chain.restype = I
-        lib.oracle_verify_tree.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, P, P, P, P, P, I]
+        lib.oracle_verify_tree.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, P, P, P, P, P, P, I]
         lib.oracle_verify_tree.restype = I
-        lib.oracle_verify_tree_lossless.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, P, P, P, P, P, I, I]
+        lib.oracle_verify_tree_lossless.argtypes = [P, P, I, P, P, P, P, P, I, I, I, I, P, P, P, P, P, P, I, I]
         lib.oracle_verify_tree_lossless.restype = I
         lib.oracle_row_stats.argtypes = [P, I, I, I, P, P, P, P, P, I]
         lib.oracle_row_stats.restype = I
@@ -88,7 +88,8 @@ def verify_chain(target, draft, draft_tokens, u_accept, u_sample, temperature, *
     u_sample [B, g+1]. Ragged: target [sum(g_b+1), V], draft [sum g_b, V],
     packed 1-D token/uniform arrays, cu_gamma [B+1], ``gamma`` = g_max.
     Returns dict(out_tokens [B, g+1], num_accepted [B], p_t, p_d (per draft row),
-    acc_margin [B], cdf_margin [B]).
+    acc_margin [B], cdf_margin [B], fallback [B]: True where the residual summed to 0 and the
+    draw fell back to P_t of the same row).
     """
     target, dt = _logits(target)
     draft, dt2 = _logits(draft)
@@ -113,19 +114,23 @@ def verify_chain(target, draft, draft_tokens, u_accept, u_sample, temperature, *
     pd = np.empty(total, np.float64)
     am = np.empty(B, np.float64)
     cm = np.empty(B, np.float64)
+    fb = np.empty(B, np.int32)
     rc = _load().oracle_verify_chain(_ptr(target), _ptr(draft), dt, _ptr(tokens), _ptr(ua), _ptr(us),
                                      _ptr(temperature), _ptr(cu), total, B, g, V, _ptr(out), _ptr(na),
-                                     _ptr(pt), _ptr(pd), _ptr(am), _ptr(cm), int(mutant), _threads(nthreads))
+                                     _ptr(pt), _ptr(pd), _ptr(am), _ptr(cm), _ptr(fb), int(mutant),
+                                     _threads(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_verify_chain failed")
-    return dict(out_tokens=out, num_accepted=na, p_t=pt, p_d=pd, acc_margin=am, cdf_margin=cm)
+    return dict(out_tokens=out, num_accepted=na, p_t=pt, p_d=pd, acc_margin=am, cdf_margin=cm,
+                fallback=fb.astype(bool))
 
 
 def verify_tree(target, draft, node_tokens, parents, u_accept, u_sample, temperature, max_depth,
                 nthreads=None):
     """Token-tree verification. target [B, N, V]; draft [B, N-1, V] (row v-1 is node v);
     node_tokens, parents, u_accept, u_sample [B, N]. Returns dict(out_tokens,
-    out_nodes [B, max_depth+1], num_accepted [B], acc_margin, cdf_margin)."""
+    out_nodes [B, max_depth+1], num_accepted [B], acc_margin, cdf_margin, fallback: True where the
+    residual at the end node summed to 0 and the draw fell back to its target row)."""
     target, dt = _logits(target)
     draft, dt2 = _logits(draft)
     assert dt == dt2
@@ -140,18 +145,21 @@ def verify_tree(target, draft, node_tokens, parents, u_accept, u_sample, tempera
     na = np.empty(B, np.int32)
     am = np.empty(B, np.float64)
     cm = np.empty(B, np.float64)
+    fb = np.empty(B, np.int32)
     rc = _load().oracle_verify_tree(_ptr(target), _ptr(draft), dt, _ptr(tok), _ptr(par), _ptr(ua), _ptr(us),
                                     _ptr(temperature), B, N, V, int(max_depth), _ptr(out), _ptr(onodes),
-                                    _ptr(na), _ptr(am), _ptr(cm), _threads(nthreads))
+                                    _ptr(na), _ptr(am), _ptr(cm), _ptr(fb), _threads(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_verify_tree failed")
-    return dict(out_tokens=out, out_nodes=onodes, num_accepted=na, acc_margin=am, cdf_margin=cm)
+    return dict(out_tokens=out, out_nodes=onodes, num_accepted=na, acc_margin=am, cdf_margin=cm,
+                fallback=fb.astype(bool))
 
 
 def verify_tree_lossless(target, draft, node_tokens, parents, u_accept, u_sample, temperature, max_depth,
                          nthreads=None, mutant=MUT_NONE):
     """Lossless multi-candidate token-tree verification (siblings tried in index order, each
-    against the residual left by the rejected ones). Same arguments and outputs as verify_tree."""
+    against the residual left by the rejected ones). Same arguments and outputs as verify_tree;
+    fallback is True where a rejected sibling's residual summed to 0 and r was kept."""
     target, dt = _logits(target)
     draft, dt2 = _logits(draft)
     assert dt == dt2
@@ -166,13 +174,15 @@ def verify_tree_lossless(target, draft, node_tokens, parents, u_accept, u_sample
     na = np.empty(B, np.int32)
     am = np.empty(B, np.float64)
     cm = np.empty(B, np.float64)
+    fb = np.empty(B, np.int32)
     rc = _load().oracle_verify_tree_lossless(_ptr(target), _ptr(draft), dt, _ptr(tok), _ptr(par), _ptr(ua),
                                              _ptr(us), _ptr(temperature), B, N, V, int(max_depth), _ptr(out),
-                                             _ptr(onodes), _ptr(na), _ptr(am), _ptr(cm), int(mutant),
+                                             _ptr(onodes), _ptr(na), _ptr(am), _ptr(cm), _ptr(fb), int(mutant),
                                              _threads(nthreads))
     if rc != 0:
         raise RuntimeError("oracle_verify_tree_lossless failed")
-    return dict(out_tokens=out, out_nodes=onodes, num_accepted=na, acc_margin=am, cdf_margin=cm)
+    return dict(out_tokens=out, out_nodes=onodes, num_accepted=na, acc_margin=am, cdf_margin=cm,
+                fallback=fb.astype(bool))
 
 
 def row_stats(logits, temperature, nthreads=None):

@@ -30,7 +30,8 @@
  *   - inverse CDF: y = min{ j : C_j > u * S } with C the running sum in
  *     ascending token order; if rounding leaves no such j, y is the last
  *     token with positive mass;
- *   - a residual whose sum underflows to 0 falls back to P_t of that row;
+ *   - a residual whose sum underflows to 0 falls back to P_t of that row (a
+ *     diagnostic flag marks such requests);
  *   - temperature 0 means greedy: accept iff the draft token is the target
  *     argmax (lowest index on ties) and emit the argmax at the first
  *     mismatch;
@@ -196,6 +197,7 @@ typedef struct {
     double *pt_diag, *pd_diag; /* [gamma] or NULL */
     double *acc_margin;        /* min |u - min(1,r)| over examined positions */
     double *cdf_margin;
+    int32_t *fallback;         /* 1 when the draw fell back to P_t (zero residual sum) */
 } chain_req;
 
 static void fail_request(int32_t *out, int width, int32_t *num_accepted)
@@ -213,6 +215,7 @@ static void verify_chain_one(const chain_req *r, double *work)
             r->pt_diag[i] = r->pd_diag[i] = NAN;
     *r->acc_margin = INFINITY;
     *r->cdf_margin = INFINITY;
+    *r->fallback = 0;
 
     /* Validation of everything the request reads. */
     int ok = temperature_usable(r->T);
@@ -318,9 +321,11 @@ static void verify_chain_one(const chain_req *r, double *work)
     double S = 0.0;
     for (int j = 0; j < V; ++j)
         S += q[j];
-    if (!(S > 0.0))
+    if (!(S > 0.0)) {
         for (int j = 0; j < V; ++j)
             q[j] = ptn[j]; /* residual underflow: fall back to P_t of row n */
+        *r->fallback = 1;
+    }
 
     double margin;
     int y = inverse_cdf(q, V, (double)r->us[n], &margin);
@@ -395,6 +400,7 @@ typedef struct {
     int B, gamma, V, mutant;
     int32_t *out, *num_accepted;
     double *pt_diag, *pd_diag, *acc_margin, *cdf_margin;
+    int32_t *fallback;
 } chain_batch;
 
 /* The packed layout describes the whole batch: it is usable only when
@@ -423,6 +429,7 @@ static void chain_task(void *p, int b, double *work)
         if (!ragged_layout_valid(cb->cu, cb->B, cb->gamma, cb->total_draft)) {
             fail_request(cb->out + (size_t)b * width, width, cb->num_accepted + b);
             cb->acc_margin[b] = cb->cdf_margin[b] = INFINITY;
+            cb->fallback[b] = 0;
             return;
         }
         gb = hi - lo;
@@ -451,24 +458,26 @@ static void chain_task(void *p, int b, double *work)
     r.pd_diag = cb->pd_diag ? cb->pd_diag + d0 : NULL;
     r.acc_margin = cb->acc_margin + b;
     r.cdf_margin = cb->cdf_margin + b;
+    r.fallback = cb->fallback + b;
     verify_chain_one(&r, work);
 }
 
 /* Dense: target [B, gamma+1, V], draft [B, gamma, V], tokens/ua [B, gamma],
  * us [B, gamma+1]; ragged (cu != NULL): packed rows, request b owns draft rows
  * cu[b]..cu[b+1]-1 and target rows cu[b]+b .. cu[b+1]+b, gamma = gamma_max.
- * out [B, gamma+1]; diag arrays are indexed like the draft rows.             */
+ * out [B, gamma+1]; diag arrays are indexed like the draft rows; fallback [B] marks
+ * the requests whose draw fell back to P_t because the residual summed to 0.  */
 int oracle_verify_chain(const void *target, const void *draft, int dtype, const int32_t *tokens,
                         const float *u_accept, const float *u_sample, const float *temperature,
                         const int32_t *cu_gamma, int total_draft, int B, int gamma, int V, int32_t *out,
                         int32_t *num_accepted, double *pt_diag, double *pd_diag, double *acc_margin,
-                        double *cdf_margin, int mutant, int nthreads)
+                        double *cdf_margin, int32_t *fallback, int mutant, int nthreads)
 {
     if (B < 0 || gamma < 0 || V < 1 || (dtype != OR_F32 && dtype != OR_BF16))
         return -1;
     chain_batch cb = {target, draft,  dtype, tokens,      u_accept,     u_sample,     temperature,
                       cu_gamma, total_draft, B, gamma, V, mutant, out, num_accepted, pt_diag,
-                      pd_diag, acc_margin, cdf_margin};
+                      pd_diag, acc_margin, cdf_margin, fallback};
     size_t work = (size_t)(2 * gamma + 2) * (size_t)V;
     return run_parallel(B, nthreads, work, chain_task, &cb);
 }
@@ -492,6 +501,8 @@ typedef struct {
     int32_t *out, *out_nodes, *num_accepted;
     double *acc_margin, *cdf_margin;
     int mutant;
+    int32_t *fallback; /* 1: zero residual sum (lowest-child rule: draw from P_t[e];
+                          lossless walk: a rejected sibling left r unchanged) */
 } tree_batch;
 
 static void tree_task(void *p, int b, double *work)
@@ -505,6 +516,7 @@ static void tree_task(void *p, int b, double *work)
     const size_t t0 = (size_t)b * N, d0 = (size_t)b * (N - 1);
     tb->acc_margin[b] = INFINITY;
     tb->cdf_margin[b] = INFINITY;
+    tb->fallback[b] = 0;
     for (int k = 0; k < width; ++k)
         onodes[k] = -1;
 
@@ -607,9 +619,11 @@ static void tree_task(void *p, int b, double *work)
         double S = 0.0;
         for (int j = 0; j < V; ++j)
             S += q[j];
-        if (!(S > 0.0))
+        if (!(S > 0.0)) {
             for (int j = 0; j < V; ++j)
-                q[j] = pte[j];
+                q[j] = pte[j]; /* residual underflow: fall back to P_t of the end node */
+            tb->fallback[b] = 1;
+        }
         double margin;
         y = inverse_cdf(q, V, (double)us[e], &margin);
         tb->cdf_margin[b] = margin;
@@ -624,13 +638,13 @@ int oracle_verify_tree(const void *target, const void *draft, int dtype, const i
                        const int32_t *parents, const float *u_accept, const float *u_sample,
                        const float *temperature, int B, int N, int V, int max_depth, int32_t *out,
                        int32_t *out_nodes, int32_t *num_accepted, double *acc_margin, double *cdf_margin,
-                       int nthreads)
+                       int32_t *fallback, int nthreads)
 {
     if (B < 0 || N < 1 || V < 1 || max_depth < 0 || (dtype != OR_F32 && dtype != OR_BF16))
         return -1;
     tree_batch tb = {target,      draft,      dtype,     tokens, parents,   u_accept,     u_sample,
                      temperature, B,          N,         V,      max_depth, out,          out_nodes,
-                     num_accepted, acc_margin, cdf_margin};
+                     num_accepted, acc_margin, cdf_margin, MUT_NONE, fallback};
     size_t work = 2 * (size_t)N + (size_t)(2 * N + 1) * (size_t)V;
     return run_parallel(B, nthreads, work, tree_task, &tb);
 }
@@ -662,6 +676,7 @@ static void tree_lossless_task(void *p, int b, double *work)
     const size_t t0 = (size_t)b * N, d0 = (size_t)b * (N - 1);
     tb->acc_margin[b] = INFINITY;
     tb->cdf_margin[b] = INFINITY;
+    tb->fallback[b] = 0;
     for (int k = 0; k < width; ++k)
         onodes[k] = -1;
 
@@ -757,6 +772,8 @@ static void tree_lossless_task(void *p, int b, double *work)
             if (Z > 0.0)
                 for (int j = 0; j < V; ++j)
                     r[j] = tb->mutant == MUT_TREE_NO_RENORM ? res[j] : res[j] / Z;
+            else
+                tb->fallback[b] = 1; /* residual underflow: r is kept */
         }
         if (accepted < 0) {
             if (tb->mutant == MUT_TREE_NO_UPDATE && nrej > 0) {
@@ -786,13 +803,13 @@ int oracle_verify_tree_lossless(const void *target, const void *draft, int dtype
                                 const int32_t *parents, const float *u_accept, const float *u_sample,
                                 const float *temperature, int B, int N, int V, int max_depth, int32_t *out,
                                 int32_t *out_nodes, int32_t *num_accepted, double *acc_margin, double *cdf_margin,
-                                int mutant, int nthreads)
+                                int32_t *fallback, int mutant, int nthreads)
 {
     if (B < 0 || N < 1 || V < 1 || max_depth < 0 || (dtype != OR_F32 && dtype != OR_BF16))
         return -1;
     tree_batch tb = {target,      draft,      dtype,     tokens, parents,   u_accept,     u_sample,
                      temperature, B,          N,         V,      max_depth, out,          out_nodes,
-                     num_accepted, acc_margin, cdf_margin, mutant};
+                     num_accepted, acc_margin, cdf_margin, mutant, fallback};
     size_t work = 2 * (size_t)N + 4 * (size_t)V;
     return run_parallel(B, nthreads, work, tree_lossless_task, &tb);
 }
