@@ -118,3 +118,22 @@ def test_first_token_follows_the_root_target_row(sv):
     stat = ((counts - n * p) ** 2 / (n * p)).sum()
     assert scipy.stats.chi2.sf(stat, V - 1) > 1e-3
     assert 0.2 < (na > 0).mean() < 0.98
+
+
+@pytest.mark.parametrize("dtype,noise", [("f32", 0.01), ("f32", 0.2), ("bf16", 0.05), ("bf16", 0.2)])
+def test_near_identical_drafts(sv, dtype, noise):
+    """Draft rows within a small noise of their parent's target row, with the first children of the
+    root and of each depth-1 node forced towards rejection (u near 1): the residual left by a rejected
+    sibling is small (about the rows' total variation), so its support and normalisation depend on the
+    exact ratio of the two rows' normalisers, not on an estimate of it."""
+    d = inputgen.tree_inputs(48, 30000, seed=81 + int(noise * 100), n_nodes=21, fanout=(4, 4, 1), dtype=dtype,
+                             noise_sd=noise)
+    d["u_accept"] = d["u_accept"].copy()
+    for b in range(d["parents"].shape[0]):
+        for v in range(1, d["parents"].shape[1]):
+            p = int(d["parents"][b, v])
+            first = min(c for c in range(1, d["parents"].shape[1]) if d["parents"][b, c] == p)
+            if v == first or (v - first) % 2 == 1:
+                d["u_accept"][b, v] = 0.999
+    _, _, na = _check(sv, d, f"near-identical {dtype} sd={noise}")
+    assert (na >= 0).all()
