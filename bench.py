@@ -89,15 +89,29 @@ def device_inputs(d, dev):
     return out
 
 
-def kernel_source_hash() -> str:
+def _hash_files(paths) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in paths:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
+def kernel_source_hash() -> str:
+    """Hash of the sources of the streaming statistics kernel."""
+    return _hash_files(KERNEL_SOURCES)
+
+
+def step_source_hash() -> str:
+    """Hash of every source of the library (any kernel of a step)."""
+    csrc = "rejection_sampling_verify_spec_amd/csrc"
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(os.path.join(ROOT, csrc)))
+    return _hash_files(files + ["include/specverify.h"])
+
+
 def host_cores() -> int:
+    """Threads for the multi-threaded oracle: the CPUs this process may run on, at most 16 (the host
+    share of one GPU on the measuring machines; nproc and the model are reported beside it)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
@@ -194,38 +208,119 @@ def oracle_call(name, d, nthreads):
                                d["temperature"], nthreads=nthreads)
 
 
-def load_traffic(name):
-    """HBM bytes per launch from committed PMC counters, if they were taken on this workload and
-    match the current kernel source."""
+def _load_pmc(name):
     if not os.path.exists(PMC_FILE):
         return None
     with open(PMC_FILE) as f:
         pmc = json.load(f)
-    if pmc.get("kernel_source_hash") != kernel_source_hash() or pmc.get("workload") != WORKLOAD_TEXT[name]:
+    return pmc if pmc.get("workload") == WORKLOAD_TEXT[name] else None
+
+
+def load_traffic(name):
+    """HBM bytes per launch of the streaming kernel from committed PMC counters, if they were taken on
+    this workload and match the current kernel source."""
+    pmc = _load_pmc(name)
+    if pmc is None or pmc.get("kernel_source_hash") != kernel_source_hash():
         return None
     return pmc.get("hbm_bytes_per_launch")
 
 
-def _timed_loop(args, sv, call, copies):
-    """Warmup, then args.steps timed calls with the library's kernel events on every
-    args.time_every-th call. Returns (elapsed s, kernel ms list, last output)."""
+def load_step_bytes(name):
+    """HBM bytes of a whole step (every kernel of the library, read + written) from committed PMC
+    counters, if they were taken on this workload and every library source is unchanged since."""
+    pmc = _load_pmc(name)
+    if pmc is None or pmc.get("step_source_hash") != step_source_hash() or "step_kernels" not in pmc:
+        return None
+    return {"total": round(pmc["step_hbm_bytes"]), "per_kernel": {k: round(v) for k, v in pmc["step_kernels"].items()},
+            "source": "rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel of known size"}
+
+
+def _percentile(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, np.float64), q)) if len(xs) else float("nan")
+
+
+def _timed_loop(args, sv, call, copies, pairs_per_call=1):
+    """Warm-up, the timed region and two untimed measurement passes.
+
+    Warm-up: args.warmup calls, with the library's kernel timing switched on once, so that its
+    event pool (created on the first enable) and every other first-use cost lie before the timed
+    region. Timed region: exactly args.steps calls bracketed by torch.cuda.synchronize() (the wall
+    clock gives `elapsed`), with one HIP event pair around the whole loop on the launch stream.
+    Then an extra pass with an event between consecutive calls (per-step durations: median, p10,
+    p90) and one with the library's kernel events on every call (at least 20 launches of the
+    timed kernel). Returns a dict."""
     import torch
-    for i in range(args.warmup):
-        call(copies[i % len(copies)])
+    n = len(copies)
+    sv.spec_verify_timing_enable(True)
+    for i in range(max(args.warmup, 1)):
+        call(copies[i % n])
+    sv.spec_verify_timing_enable(False)
     torch.cuda.synchronize()
     sv.spec_verify_timing_reset()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start = time.perf_counter()
+    e0.record(stream)
     outs = None
     for i in range(args.steps):
-        timed = i % args.time_every == 0
-        if timed:
-            sv.spec_verify_timing_enable(True)
-        outs = call(copies[i % len(copies)])
-        if timed:
-            sv.spec_verify_timing_enable(False)
+        outs = call(copies[i % n])
+    e1.record(stream)
     torch.cuda.synchronize()
-    return time.perf_counter() - start, sv.spec_verify_timing_read(args.steps), outs
+    elapsed = time.perf_counter() - start
+    gpu_ms = e0.elapsed_time(e1)
+
+    nd = max(20, min(args.steps, 200))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nd + 1)]
+    evs[0].record(stream)
+    for i in range(nd):
+        call(copies[i % n])
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(nd)]
+
+    nk = max(20, min(args.steps, 200))
+    sv.spec_verify_timing_enable(True)
+    for i in range(nk):
+        call(copies[i % n])
+    sv.spec_verify_timing_enable(False)
+    torch.cuda.synchronize()
+    k_ms = sv.spec_verify_timing_read(nk * pairs_per_call)
+    sv.spec_verify_timing_reset()
+    return {"elapsed": elapsed, "gpu_ms": gpu_ms, "step_ms": step_ms, "k_ms": k_ms, "outs": outs}
+
+
+def _step_stats(t, steps):
+    """Per-step figures of a _timed_loop result for the JSON line."""
+    return {
+        "ms_per_step_gpu_events": round(t["gpu_ms"] / steps, 5),
+        "step_ms_distribution": {"median": round(_percentile(t["step_ms"], 50), 5),
+                                 "p10": round(_percentile(t["step_ms"], 10), 5),
+                                 "p90": round(_percentile(t["step_ms"], 90), 5),
+                                 "samples": len(t["step_ms"]),
+                                 "how": "extra pass after the timed region, one HIP event between consecutive "
+                                        "calls on the launch stream"},
+    }
+
+
+def host_info(threads):
+    """Host CPU facts for the CPU baseline: logical CPUs, CPUs this process may run on, model, and the
+    oracle's thread count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except AttributeError:
+        aff = os.cpu_count() or 1
+    return {"nproc": os.cpu_count(), "cpus_allowed": aff, "cpu_model": model, "threads": threads}
 
 
 def kv_copied_positions(d):
@@ -282,7 +377,8 @@ def run_cache_bench(args):
         kernel, unit, dtype = "k_draft_window", "windowed requests/s", "int32"
         metric = "windowed requests/s + table HBM GB/s, B=256 W=2048 block 128"
 
-    elapsed, k_ms, outs = _timed_loop(args, sv, call, copies)
+    tl = _timed_loop(args, sv, call, copies)
+    elapsed, k_ms, outs = tl["elapsed"], tl["k_ms"], tl["outs"]
     print(f"bench: {args.steps} steps in {elapsed * 1e3:.2f} ms", file=sys.stderr, flush=True)
     k_avg_ms = float(np.mean(k_ms)) if k_ms else float("nan")
     k_gbps = algo / (k_avg_ms * 1e-3) / 1e9
@@ -361,14 +457,15 @@ def run_cache_bench(args):
             "algorithmic_bytes_per_launch": algo,
             "avg_launch_ms": round(k_avg_ms, 5),
             "launches_timed": len(k_ms),
-            "timed_every_nth_step": args.time_every,
+            "launches_timed_how": "extra pass after the timed region, HIP events on the launch stream",
         },
         "cpu_baseline": None if cpu_calls == 0 else {
             "value": round(cpu_units / cpu_s, 1), "unit": unit, "cores": cores, "kind": "oracle",
-            "sample": sample,
+            "sample": sample, **host_info(cores),
         },
         "parity_vs_oracle": parity_ok,
     }
+    line.update(_step_stats(tl, args.steps))
     print(json.dumps(line), flush=True)
     return 0 if parity_ok is not False else 1
 
@@ -406,27 +503,8 @@ def run_bench(args):
     call = make_call(sv, name, copies[0], d)
     positions, formula_bytes, k1_bytes = workload_accounting(name, d)
 
-    for i in range(args.warmup):
-        call(copies[i % len(copies)])
-    torch.cuda.synchronize()
-
-    # HIP event pairs around the row-statistics kernel on every `time_every`-th timed step: an
-    # event pair holds the stream for a few microseconds, so recording it on every step would
-    # inflate the step time it sits in
-    sv.spec_verify_timing_reset()
-    torch.cuda.synchronize()
-    start = time.perf_counter()
-    outs = None
-    for i in range(args.steps):
-        timed = i % args.time_every == 0
-        if timed:
-            sv.spec_verify_timing_enable(True)
-        outs = call(copies[i % len(copies)])
-        if timed:
-            sv.spec_verify_timing_enable(False)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - start
-    k1_ms = sv.spec_verify_timing_read(args.steps)
+    tl = _timed_loop(args, sv, call, copies, pairs_per_call=2 if name == "tree_lossless" else 1)
+    elapsed, k1_ms, outs = tl["elapsed"], tl["k_ms"], tl["outs"]
     print(f"bench: {args.steps} steps in {elapsed * 1e3:.2f} ms", file=sys.stderr, flush=True)
 
     ms_per_step = elapsed * 1e3 / args.steps
@@ -442,11 +520,11 @@ def run_bench(args):
                            [copies[0]["target"], copies[0]["draft"]])
 
     # CPU oracle on the host cores: whole verify steps of the same batch, repeated until about
-    # args.cpu_seconds of wall time have passed (at least one step)
+    # args.cpu_seconds of wall time have passed (at least one step), then on one thread
     cores = host_cores()
     ref = None
-    cpu_steps = 0
-    cpu_s = 0.0
+    cpu_steps = cpu1_steps = 0
+    cpu_s = cpu1_s = 0.0
     if not args.skip_cpu_baseline:
         tc = time.perf_counter()
         while cpu_steps == 0 or cpu_s < args.cpu_seconds:
@@ -454,6 +532,12 @@ def run_bench(args):
             cpu_steps += 1
             cpu_s = time.perf_counter() - tc
         print(f"bench: oracle {cpu_steps} steps in {cpu_s:.2f} s on {cores} threads", file=sys.stderr, flush=True)
+        tc = time.perf_counter()
+        while cpu1_steps == 0 or cpu1_s < args.cpu1_seconds:
+            oracle_call(name, d, 1)
+            cpu1_steps += 1
+            cpu1_s = time.perf_counter() - tc
+        print(f"bench: oracle {cpu1_steps} steps in {cpu1_s:.2f} s on 1 thread", file=sys.stderr, flush=True)
     sample = name == "sample"
     if sample:
         tok = outs.cpu().numpy()
@@ -466,6 +550,7 @@ def run_bench(args):
     unit = "sampled draft tokens/s" if sample else "verified draft positions/s"
     what = "sampling calls" if sample else "full verify steps"
     per = "rows" if sample else "positions"
+    in_dt = "bf16" if d["logits" if sample else "target"].dtype == np.uint16 else "f32"
 
     line = {
         "metric": SAMPLE_METRIC if sample else (METRIC if name == "large" else
@@ -479,8 +564,11 @@ def run_bench(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
+        # arithmetic of the path: the streaming statistics (nearly all of the time) in fp32, the
+        # acceptance scan and the draw in fp64; the logits are read as stored (input_dtype)
         "dtype": "f32",
-        "input_dtype": "bf16" if d["logits" if sample else "target"].dtype == np.uint16 else "f32",
+        "arith": "fp32 streaming statistics; fp64 acceptance scan and draw",
+        "input_dtype": in_dt,
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[name], "B": int(d["temperature"].shape[0]),
                    "V": int(d["logits" if sample else "target"].shape[-1]), "positions_per_step": positions,
@@ -488,6 +576,7 @@ def run_bench(args):
         "logits_gbps_formula": round(gbps, 1),
         "hbm_peak_frac_formula": round(gbps / HBM_PEAK_GBPS, 4),
         "formula_bytes_per_step": formula_bytes,
+        "measured_bytes_per_step": load_step_bytes(name),
         "roofline": {
             "bound": "hbm",
             "kernel": KERNEL,
@@ -499,7 +588,7 @@ def run_bench(args):
             "algorithmic_bytes_per_launch": k1_bytes,
             "avg_launch_ms": round(k1_avg_ms, 5),
             "launches_timed": len(k1_ms),
-            "timed_every_nth_step": args.time_every,
+            "launches_timed_how": "extra pass after the timed region, HIP events on the launch stream",
         },
         "cpu_baseline": None if ref is None else {
             "value": round(positions * cpu_steps / cpu_s, 1),
@@ -507,13 +596,17 @@ def run_bench(args):
             "cores": cores,
             "kind": "oracle",
             "sample": f"{cpu_steps} {what} of the same batch ({positions} {per} each), "
-                      f"fp64 oracle, {cores} threads, {cpu_s:.2f} s wall",
+                      f"fp64 oracle, {cores} threads, {cpu_s:.2f} s wall; then {cpu1_steps} on 1 thread, "
+                      f"{cpu1_s:.2f} s wall",
+            "single_thread_value": round(positions * cpu1_steps / cpu1_s, 1),
+            **host_info(cores),
         },
         "parity_vs_oracle": parity_ok,
         "read_ceiling": {"kernel": "k_read_probe", "gbps": round(ceiling, 1),
                          "frac_of_peak": round(ceiling / HBM_PEAK_GBPS, 4),
                          "row_stats_frac_of_ceiling": round(k1_gbps / ceiling, 4)},
     }
+    line.update(_step_stats(tl, args.steps))
     if not sample:
         line["mean_num_accepted"] = round(float(np.mean(na[na >= 0])), 4)
     if walk_ms:
@@ -526,7 +619,8 @@ def run_bench(args):
             "bound": "hbm", "kernel": "k_tree_lossless", "achieved": round(wb / (walk_avg * 1e-3) / 1e9, 1),
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(wb / (walk_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "traffic": None, "algorithmic_bytes_per_launch": wb, "avg_launch_ms": round(walk_avg, 5),
-            "launches_timed": len(walk_ms), "timed_every_nth_step": args.time_every,
+            "launches_timed": len(walk_ms),
+            "launches_timed_how": "extra pass after the timed region, HIP events on the launch stream",
         }
     print(json.dumps(line), flush=True)
     return 0 if parity_ok is not False else 1
@@ -596,6 +690,15 @@ def write_pmc(dirs, workload):
         "traffic_over_algorithmic": (fetch_b + write_b) / algo,
         "kernel_source_hash": kernel_source_hash(),
     }
+    # every library kernel of the step (the read-ceiling probe is a measurement aid, not a step)
+    fa, wa = _counter_avgs(fetch_dir), _counter_avgs(write_dir)
+    step = {}
+    for (k, c), v in fa.items():
+        if c == "FETCH_SIZE" and (k.startswith("void sv::") or k.startswith("sv::")):
+            step[k] = v * f_scale + wa.get((k, "WRITE_SIZE"), 0.0) * w_scale
+    out["step_kernels"] = step
+    out["step_hbm_bytes"] = sum(step.values())
+    out["step_source_hash"] = step_source_hash()
     os.makedirs(os.path.dirname(PMC_FILE), exist_ok=True)
     with open(PMC_FILE, "w") as f:
         json.dump(out, f, indent=1)
@@ -641,9 +744,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="large", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
-    ap.add_argument("--time-every", type=int, default=16,
-                    help="record the row-statistics kernel's HIP events on every N-th timed step")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall time spent timing the CPU oracle")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="wall time spent timing the CPU oracle on the host cores")
+    ap.add_argument("--cpu1-seconds", type=float, default=4.0,
+                    help="wall time spent timing the CPU oracle on one thread")
     ap.add_argument("--skip-cpu-baseline", action="store_true", help="no oracle run (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--summarize-rocprof", metavar="DIR")
