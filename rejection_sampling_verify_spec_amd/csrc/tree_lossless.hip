@@ -75,6 +75,17 @@ struct LLSpace {
 
 __device__ __forceinline__ uint64_t f64_bits(double v) { return (uint64_t)__double_as_longlong(v); }
 
+// One residual step at one token, max(0, R - s e), with the product rounded on
+// its own (no fused multiply-add): when a rejected sibling's draft row equals
+// the current distribution, R = fl(e' izt) and s e round to the same value and
+// the step gives exactly 0, so the residual sum is 0 and r is kept, as in the
+// definition. A fused form would leave the rounding error of R instead.
+__device__ __forceinline__ double residual_step(double R, double s, double e) {
+#pragma clang fp contract(off)
+  const double se = s * e;
+  return fmax(0.0, R - se);
+}
+
 // Segment sums of pass buffer `buf` read by one wave, kSegLoads per lane at a
 // time with all loads in flight: lane l holds segments l + 64 k at v[k].
 constexpr int kSegLoads = 8;
@@ -121,18 +132,18 @@ __device__ __forceinline__ void child_test(const LLArgs& A, LLSpace& P, long lon
       double m = 0.0;
       if (l == 0) {
         const float lt = Elem<DT>::at(A.tgt, (t0 + v) * (long long)A.V + x);
-        m = emass_t(lt, P.mt[v], c64, c32, P.tab) / P.zt[v];
+        m = emass_t(lt, P.mt[v], c64, c32, P.tab) * (1.0 / P.zt[v]);
       } else if (l < nrej + 2) {
         const int w = l <= nrej ? P.rej[l - 1] : c;
         const float ld = Elem<DT>::at(A.dft, (d0 + w - 1) * (long long)A.V + x);
-        m = emass_t(ld, P.md[w], c64, c32, P.tab) / P.zd[w];
+        m = emass_t(ld, P.md[w], c64, c32, P.tab) * (1.0 / P.zd[w]);
       }
       const int n = min(64, nrej + 2 - l0);
       for (int k = 0; k < n; ++k) {
         const double mk = lane_f64(m, k);
         const int idx = l0 + k;
         if (idx == 0) R = mk;
-        else if (idx <= nrej) R = P.skip[idx - 1] ? R : fmax(0.0, R - P.S[idx - 1] * mk);
+        else if (idx <= nrej) R = P.skip[idx - 1] ? R : residual_step(R, P.S[idx - 1], mk);
         else q = mk;
       }
     }
@@ -208,7 +219,7 @@ __device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P,
       float x[epv];
       unpack<DT>(w[i], x);
 #pragma unroll
-      for (int e = 0; e < epv; ++e) R[i * epv + e] = fmax(0.0, R[i * epv + e] - s * emass_t(x[e], md, c64, c32, P.tab));
+      for (int e = 0; e < epv; ++e) R[i * epv + e] = residual_step(R[i * epv + e], s, emass_t(x[e], md, c64, c32, P.tab));
     }
     k = k2;
   }
