@@ -245,19 +245,29 @@ def _timed_loop(args, sv, call, copies, pairs_per_call=1):
 
     Warm-up: args.warmup calls, with the library's kernel timing switched on once, so that its
     event pool (created on the first enable) and every other first-use cost lie before the timed
-    region. Timed region: exactly args.steps calls bracketed by torch.cuda.synchronize() (the wall
+    region; then untimed calls until args.settle_ms have passed (GPU clocks). Timed region: exactly args.steps calls bracketed by torch.cuda.synchronize() (the wall
     clock gives `elapsed`), with one HIP event pair around the whole loop on the launch stream.
     Then an extra pass with an event between consecutive calls (per-step durations: median, p10,
     p90) and one with the library's kernel events on every call (at least 20 launches of the
     timed kernel). Returns a dict."""
     import torch
     n = len(copies)
+    t_warm = time.perf_counter()
     sv.spec_verify_timing_enable(True)
     for i in range(max(args.warmup, 1)):
         call(copies[i % n])
     sv.spec_verify_timing_enable(False)
     torch.cuda.synchronize()
     sv.spec_verify_timing_reset()
+    # settle: more untimed calls until args.settle_ms of wall time have passed since the warm-up
+    # began, so that the GPU's clocks have left their idle state (a few warm-up calls of a
+    # fraction of a millisecond each do not get there)
+    settle = 0
+    while (time.perf_counter() - t_warm) * 1e3 < args.settle_ms:
+        for _ in range(20):
+            call(copies[settle % n])
+            settle += 1
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -288,12 +298,14 @@ def _timed_loop(args, sv, call, copies, pairs_per_call=1):
     torch.cuda.synchronize()
     k_ms = sv.spec_verify_timing_read(nk * pairs_per_call)
     sv.spec_verify_timing_reset()
-    return {"elapsed": elapsed, "gpu_ms": gpu_ms, "step_ms": step_ms, "k_ms": k_ms, "outs": outs}
+    return {"elapsed": elapsed, "gpu_ms": gpu_ms, "step_ms": step_ms, "k_ms": k_ms, "outs": outs,
+            "settle_calls": settle}
 
 
 def _step_stats(t, steps):
     """Per-step figures of a _timed_loop result for the JSON line."""
     return {
+        "settle_calls": t["settle_calls"],
         "ms_per_step_gpu_events": round(t["gpu_ms"] / steps, 5),
         "step_ms_distribution": {"median": round(_percentile(t["step_ms"], 50), 5),
                                  "p10": round(_percentile(t["step_ms"], 10), 5),
@@ -744,6 +756,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="large", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--copies", type=int, default=3, help="input copies rotated across steps")
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="untimed calls after the warm-up until this much wall time has passed since it began")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="wall time spent timing the CPU oracle on the host cores")
     ap.add_argument("--cpu1-seconds", type=float, default=4.0,
