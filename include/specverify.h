@@ -21,7 +21,8 @@
  * Conventions shared by every entry point
  *   - All array arguments are DEVICE pointers owned by the caller. The
  *     library never allocates, frees or retains them, and keeps no per-call
- *     state; scratch memory is the caller's `workspace`.
+ *     state; scratch memory is the caller's `workspace` (spec_verify_noalloc
+ *     instead uses a fixed array that the library holds on each device).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default
  *     stream). Outputs are valid after the caller synchronises that stream.
  *   - Logits are row-major with the vocabulary contiguous; `dtype` is
@@ -64,6 +65,7 @@ typedef enum sv_status {
     SV_ENOWS = -3,   /* workspace null, too small or not 256-byte aligned       */
     SV_EALIGN = -4,  /* a logits pointer not aligned to its element size        */
     SV_EHIP = -5,    /* a HIP runtime call or kernel launch failed              */
+    SV_ESCRATCH = -6, /* spec_verify_noalloc: the sizes need more than its scratch */
 } sv_status;
 
 typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
@@ -74,6 +76,7 @@ typedef enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 #define SV_MAX_VOCAB (1 << 28)
 #define SV_MAX_KV_SLOTS (1 << 30)     /* sink + window slots of one KV cache      */
 #define SV_MAX_KV_ROW_BYTES (1 << 30) /* bytes of one cache row (one head, one position) */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20) /* scratch of spec_verify_noalloc, per device */
 
 /* Workspace bytes needed by spec_verify for these sizes (0 on bad sizes). */
 size_t spec_verify_workspace_bytes(int32_t B, int32_t gamma, int32_t V, int32_t dtype);
@@ -103,6 +106,24 @@ int spec_verify(const void* target_logits, const void* draft_logits, int32_t dty
                 const float* temperature, int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
                 int32_t* num_accepted, float* diag_probs, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/*
+ * spec_verify for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. The same
+ * arguments (without the workspace), results and errors as spec_verify; it
+ * calls no allocating routine. Its scratch is a fixed array of
+ * SV_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on every device it
+ * runs on until the process ends (its address is looked up on the first call on
+ * a device). Sizes whose workspace (spec_verify_workspace_bytes) exceeds it
+ * return SV_ESCRATCH before anything is enqueued. Every call on a device uses
+ * that device's one array: calls that overlap on one device (on different
+ * streams, or from different threads) race and must be serialised by the caller;
+ * calls in one stream are ordered and safe.
+ */
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits, int32_t dtype,
+                        const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                        const float* temperature, int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
+                        int32_t* num_accepted, float* diag_probs, void* stream);
 
 /* Workspace bytes for spec_verify_ragged. */
 size_t spec_verify_ragged_workspace_bytes(int32_t B, int32_t total_draft, int32_t gamma_max, int32_t V,

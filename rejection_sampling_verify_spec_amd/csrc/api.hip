@@ -28,6 +28,15 @@ hipError_t launch_read_probe(const void* src, long long nvec, uint32_t* out, hip
 }  // namespace svp
 
 static_assert(sizeof(Partial) == 8, "Partial layout");
+
+// ---- scratch of the allocation-free entry point
+// A fixed array in every device's copy of the library's code object, held until
+// the process ends. In host code `scratch` names a host-side stand-in, never the
+// device memory: kernels and copies take the address that hipGetSymbolAddress
+// returns for the current device (each device has its own copy of the array).
+constexpr size_t kScratchBytes = SV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 static_assert(sizeof(TileRec) == 128, "TileRec layout");
 
 namespace {
@@ -128,6 +137,28 @@ int launch_chain(int dt, const void* tgt, const void* dft, int V, const Layout& 
   return e == hipSuccess ? SV_OK : SV_EHIP;
 }
 
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's scratch address, looked up once per device (with that
+// device current) on its first call.
+int scratch_for_current_device(char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_EHIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SV_EHIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = static_cast<char*>(p);
+  return SV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -193,16 +224,27 @@ static int check_ws(const void* ws, size_t have, size_t need) {
   return SV_OK;
 }
 
-int spec_verify(const void* target_logits, const void* draft_logits, int32_t dtype, const int32_t* draft_tokens,
-                const float* u_accept, const float* u_sample, const float* temperature, int32_t B, int32_t gamma,
-                int32_t V, int32_t* out_tokens, int32_t* num_accepted, float* diag_probs, void* workspace,
-                size_t workspace_bytes, void* stream) {
+// Argument checks of the dense chain entry points (everything but the workspace).
+static int check_chain_args(const void* target_logits, const void* draft_logits, int32_t dtype,
+                            const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                            const float* temperature, int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
+                            int32_t* num_accepted) {
   if (B < 0 || gamma < 0 || gamma > SV_MAX_GAMMA) return SV_EINVAL;
   if (B == 0) return SV_OK;
   int rc = check_common(target_logits, draft_logits, gamma > 0, dtype, V);
   if (rc) return rc;
   if (!u_sample || !temperature || !out_tokens || !num_accepted) return SV_EINVAL;
   if (gamma > 0 && (!draft_tokens || !u_accept)) return SV_EINVAL;
+  return SV_OK;
+}
+
+int spec_verify(const void* target_logits, const void* draft_logits, int32_t dtype, const int32_t* draft_tokens,
+                const float* u_accept, const float* u_sample, const float* temperature, int32_t B, int32_t gamma,
+                int32_t V, int32_t* out_tokens, int32_t* num_accepted, float* diag_probs, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int rc = check_chain_args(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sample, temperature, B,
+                            gamma, V, out_tokens, num_accepted);
+  if (rc || B == 0) return rc;
   const long long RT = (long long)B * (gamma + 1), RD = (long long)B * gamma;
   Carve cv = carve(RT + RD, B, V, dtype);
   rc = check_ws(workspace, workspace_bytes, cv.total);
@@ -211,6 +253,25 @@ int spec_verify(const void* target_logits, const void* draft_logits, int32_t dty
   return launch_chain(dtype, target_logits, draft_logits, V, L, draft_tokens, u_accept, u_sample, temperature,
                       out_tokens, gamma + 1, num_accepted, diag_probs, static_cast<char*>(workspace), cv,
                       static_cast<hipStream_t>(stream));
+}
+
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits, int32_t dtype,
+                        const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                        const float* temperature, int32_t B, int32_t gamma, int32_t V, int32_t* out_tokens,
+                        int32_t* num_accepted, float* diag_probs, void* stream) {
+  int rc = check_chain_args(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sample, temperature, B,
+                            gamma, V, out_tokens, num_accepted);
+  if (rc || B == 0) return rc;
+  const long long RT = (long long)B * (gamma + 1), RD = (long long)B * gamma;
+  const Carve cv = carve(RT + RD, B, V, dtype);
+  if (cv.total > kScratchBytes) return SV_ESCRATCH;
+  char* ws = nullptr;
+  if ((rc = scratch_for_current_device(&ws))) return rc;
+  // nothing in the scratch needs clearing: the streaming kernel writes every
+  // partial and zeroes the per-request counters before the tail kernel reads them
+  Layout L{LAYOUT_DENSE, B, gamma, nullptr, 0, RT, RD};
+  return launch_chain(dtype, target_logits, draft_logits, V, L, draft_tokens, u_accept, u_sample, temperature,
+                      out_tokens, gamma + 1, num_accepted, diag_probs, ws, cv, static_cast<hipStream_t>(stream));
 }
 
 int spec_verify_ragged(const void* target_logits, const void* draft_logits, int32_t dtype, const int32_t* cu_gamma,
@@ -433,6 +494,7 @@ const char* spec_verify_strerror(int status) {
     case SV_ENOWS: return "workspace missing, too small or not 256-byte aligned";
     case SV_EALIGN: return "logits pointer not aligned to its element size";
     case SV_EHIP: return "HIP runtime or kernel launch failure";
+    case SV_ESCRATCH: return "sizes need more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }

@@ -20,7 +20,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # the in-tree build; SPECVERIFY_LIB names another build of the same library
 LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(_HERE, "libspecverify.so")
 
-SV_OK, SV_EINVAL, SV_EDTYPE, SV_ENOWS, SV_EALIGN, SV_EHIP = 0, -1, -2, -3, -4, -5
+SV_OK, SV_EINVAL, SV_EDTYPE, SV_ENOWS, SV_EALIGN, SV_EHIP, SV_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
+SV_NOALLOC_SCRATCH_BYTES = 32 << 20
 SV_F32, SV_BF16 = 0, 1
 
 if not os.path.exists(LIB_PATH):
@@ -40,6 +41,8 @@ _lib.spec_row_softmax_stats_workspace_bytes.argtypes = [_I32, _I32, _I32]
 _lib.spec_row_softmax_stats_workspace_bytes.restype = _SZ
 _lib.spec_verify.argtypes = [_P, _P, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]
 _lib.spec_verify.restype = ctypes.c_int
+_lib.spec_verify_noalloc.argtypes = [_P, _P, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P]
+_lib.spec_verify_noalloc.restype = ctypes.c_int
 _lib.spec_verify_ragged.argtypes = [_P, _P, _I32, _P, _I32, _P, _P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _SZ,
                                     _P]
 _lib.spec_verify_ragged.restype = ctypes.c_int
@@ -148,6 +151,13 @@ def spec_verify(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sa
     return _lib.spec_verify(_ptr(target_logits), _ptr(draft_logits), dtype, _ptr(draft_tokens), _ptr(u_accept),
                             _ptr(u_sample), _ptr(temperature), B, gamma, V, _ptr(out_tokens), _ptr(num_accepted),
                             _ptr(diag_probs), _ptr(workspace), workspace_bytes, stream)
+
+
+def spec_verify_noalloc(target_logits, draft_logits, dtype, draft_tokens, u_accept, u_sample, temperature, B, gamma,
+                        V, out_tokens, num_accepted, diag_probs, stream) -> int:
+    return _lib.spec_verify_noalloc(_ptr(target_logits), _ptr(draft_logits), dtype, _ptr(draft_tokens),
+                                    _ptr(u_accept), _ptr(u_sample), _ptr(temperature), B, gamma, V, _ptr(out_tokens),
+                                    _ptr(num_accepted), _ptr(diag_probs), stream)
 
 
 def spec_verify_ragged(target_logits, draft_logits, dtype, cu_gamma, total_draft, draft_tokens, u_accept, u_sample,
