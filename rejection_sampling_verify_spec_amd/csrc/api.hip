@@ -42,12 +42,19 @@ static_assert(sizeof(TileRec) == 128, "TileRec layout");
 namespace {
 
 // Chunk of a row handled by one row-statistics workgroup, in 16-byte vectors
-// (a multiple of kTPB * kU). Fixed per process; SPECVERIFY_CHUNK_VECS overrides it.
-int chunk_vecs() {
-  static std::atomic<int> cached{0};
+// (a multiple of kTPB * kU). Calls over many rows take 2048 vectors (32 KB of
+// logits per workgroup); calls whose rows would then give fewer than 8192
+// workgroups (four per resident slot of a 256-CU part at eight per CU) take
+// 1024, so that small batches still spread over every CU and their last round
+// of workgroups is short. The choice depends only on the call's sizes, so the
+// workspace queries and the calls agree. SPECVERIFY_CHUNK_VECS overrides it.
+int per_vec(int dt) { return dt == SV_BF16 ? 8 : 4; }
+
+int env_chunk_vecs() {
+  static std::atomic<int> cached{-1};
   int v = cached.load(std::memory_order_relaxed);
-  if (v) return v;
-  v = 2 * kTPB * kU;
+  if (v >= 0) return v;
+  v = 0;
   if (const char* e = getenv("SPECVERIFY_CHUNK_VECS")) {
     int x = atoi(e);
     if (x >= kTPB * kU && x % (kTPB * kU) == 0 && x <= (1 << 22)) v = x;
@@ -56,13 +63,17 @@ int chunk_vecs() {
   return v;
 }
 
-int per_vec(int dt) { return dt == SV_BF16 ? 8 : 4; }
+struct Chunking {
+  int cv;   // 16-byte vectors per chunk
+  int nch;  // chunks per row
+};
 
-int nchunk_for(int V, int dt) {
-  int nvec = V / per_vec(dt);
-  int cv = chunk_vecs();
-  int n = (nvec + cv - 1) / cv;
-  return n < 1 ? 1 : n;
+Chunking chunking(long long rows, int V, int dt) {
+  const int nvec = V / per_vec(dt);
+  auto nch_of = [&](int cv) { const int n = (nvec + cv - 1) / cv; return n < 1 ? 1 : n; };
+  int cv = env_chunk_vecs();
+  if (!cv) cv = rows * nch_of(2 * kTPB * kU) < 8192 ? kTPB * kU : 2 * kTPB * kU;
+  return Chunking{cv, nch_of(cv)};
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -75,7 +86,7 @@ struct Carve {
 
 Carve carve(long long rows, int B, int V, int dt) {
   Carve c;
-  const int nchunk = nchunk_for(V, dt);
+  const int nchunk = chunking(rows, V, dt).nch;
   const int ntile = tiles_per_row(V, dt);
   c.part = 0;
   c.jobs = align256((size_t)rows * nchunk * sizeof(Partial));
@@ -115,9 +126,9 @@ void timing_mark(hipStream_t st, bool start) {
 
 int launch_stats(int dt, const void* tgt, const void* dft, int V, const Layout& L, const float* temperature,
                  Partial* part, hipStream_t st, int* zero_counts = nullptr) {
+  const Chunking ch = chunking(L.RT + L.RD, V, dt);
   timing_mark(st, true);
-  hipError_t e =
-      launch_row_stats(dt, tgt, dft, V, L, temperature, chunk_vecs(), nchunk_for(V, dt), part, zero_counts, st);
+  hipError_t e = launch_row_stats(dt, tgt, dft, V, L, temperature, ch.cv, ch.nch, part, zero_counts, st);
   timing_mark(st, false);
   return e == hipSuccess ? SV_OK : SV_EHIP;
 }
@@ -131,8 +142,9 @@ int launch_chain(int dt, const void* tgt, const void* dft, int V, const Layout& 
   int* done = reinterpret_cast<int*>(ws + cv.done);
   int rc = launch_stats(dt, tgt, dft, V, L, temperature, part, st, done);
   if (rc) return rc;
-  hipError_t e = launch_verify_chain(dt, tgt, dft, V, L, tokens, ua, us, temperature, part, nchunk_for(V, dt),
-                                     chunk_vecs(), reinterpret_cast<TileRec*>(ws + cv.recs), done, out, out_width,
+  const Chunking ch = chunking(L.RT + L.RD, V, dt);
+  hipError_t e = launch_verify_chain(dt, tgt, dft, V, L, tokens, ua, us, temperature, part, ch.nch,
+                                     ch.cv, reinterpret_cast<TileRec*>(ws + cv.recs), done, out, out_width,
                                      num_acc, diag, force_exact_residual(), st);
   return e == hipSuccess ? SV_OK : SV_EHIP;
 }
@@ -190,7 +202,8 @@ struct CarveLL {
 static CarveLL carve_ll(int B, int N, int V, int dt) {
   CarveLL c;
   c.part = 0;
-  c.sums = align256((size_t)B * (2 * N - 1) * nchunk_for(V, dt) * sizeof(Partial));
+  const long long rows = (long long)B * (2 * N - 1);
+  c.sums = align256((size_t)rows * chunking(rows, V, dt).nch * sizeof(Partial));
   c.ctr = c.sums + align256((size_t)B * 2 * lossless_segments(V, dt) * sizeof(double));
   c.total = c.ctr + align256((size_t)B * sizeof(int));
   return c;
@@ -208,7 +221,7 @@ size_t spec_sample_rows_workspace_bytes(int32_t rows, int32_t V, int32_t dtype) 
 
 size_t spec_row_softmax_stats_workspace_bytes(int32_t rows, int32_t V, int32_t dtype) {
   if (rows < 0 || V < 1 || V > SV_MAX_VOCAB || (dtype != 0 && dtype != 1)) return 0;
-  return align256((size_t)rows * nchunk_for(V, dtype) * sizeof(Partial));
+  return align256((size_t)rows * chunking(rows, V, dtype).nch * sizeof(Partial));
 }
 
 static int check_common(const void* tgt, const void* dft, bool need_dft, int32_t dtype, int32_t V) {
@@ -320,10 +333,12 @@ int spec_verify_tree(const void* target_logits, const void* draft_logits, int32_
   int* done = reinterpret_cast<int*>(ws + cv.done);
   if ((rc = launch_stats(dtype, target_logits, draft_logits, V, L, temperature, part, st, done))) return rc;
   if (launch_accept_tree(dtype, target_logits, draft_logits, V, L, max_depth, node_tokens, parents, u_accept,
-                         u_sample, temperature, part, nchunk_for(V, dtype), out_tokens, out_nodes, num_accepted,
+                         u_sample, temperature, part, chunking(RT + RD, V, dtype).nch, out_tokens, out_nodes,
+                         num_accepted,
                          jobs, st) != hipSuccess)
     return SV_EHIP;
-  if (launch_finish_jobs(dtype, target_logits, draft_logits, V, B, jobs, recs, part, nchunk_for(V, dtype), RT, done,
+  if (launch_finish_jobs(dtype, target_logits, draft_logits, V, B, jobs, recs, part, chunking(RT + RD, V, dtype).nch,
+                         RT, done,
                          out_tokens, max_depth + 1, force_exact_residual(), st) != hipSuccess)
     return SV_EHIP;
   return SV_OK;
@@ -354,7 +369,8 @@ int spec_verify_tree_lossless(const void* target_logits, const void* draft_logit
   if ((rc = launch_stats(dtype, target_logits, draft_logits, V, L, temperature, part, st, ctr))) return rc;
   timing_mark(st, true);
   const hipError_t e = launch_tree_lossless(dtype, target_logits, draft_logits, V, L, max_depth, node_tokens, parents,
-                                            u_accept, u_sample, temperature, part, nchunk_for(V, dtype), sums, ctr,
+                                            u_accept, u_sample, temperature, part, chunking(RT + RD, V, dtype).nch,
+                                            sums, ctr,
                                             out_tokens, out_nodes, num_accepted, st);
   timing_mark(st, false);
   return e == hipSuccess ? SV_OK : SV_EHIP;
@@ -374,7 +390,8 @@ int spec_row_softmax_stats(const void* logits, int32_t dtype, int32_t rows, int3
   Partial* part = static_cast<Partial*>(workspace);
   Layout L{LAYOUT_ROWS, rows, 0, nullptr, 0, rows, 0};
   if ((rc = launch_stats(dtype, logits, nullptr, V, L, temperature, part, st))) return rc;
-  if (launch_stats_finalize(part, nchunk_for(V, dtype), rows, temperature, out_max, out_logz, out_argmax, st) !=
+  if (launch_stats_finalize(part, chunking(rows, V, dtype).nch, rows, temperature, out_max, out_logz, out_argmax,
+                            st) !=
       hipSuccess)
     return SV_EHIP;
   return SV_OK;
@@ -398,10 +415,11 @@ int spec_sample_rows(const void* logits, int32_t dtype, int32_t rows, int32_t V,
   int* done = reinterpret_cast<int*>(ws + cv.done);
   Layout L{LAYOUT_ROWS, rows, 0, nullptr, 0, rows, 0};
   if ((rc = launch_stats(dtype, logits, nullptr, V, L, temperature, part, st, done))) return rc;
-  if (launch_sample_jobs(dtype, logits, V, part, nchunk_for(V, dtype), chunk_vecs(), rows, temperature, u, jobs,
+  const Chunking ch = chunking(rows, V, dtype);
+  if (launch_sample_jobs(dtype, logits, V, part, ch.nch, ch.cv, rows, temperature, u, jobs,
                          out_tokens, st) != hipSuccess)
     return SV_EHIP;
-  if (launch_finish_jobs(dtype, logits, logits, V, rows, jobs, recs, part, nchunk_for(V, dtype), rows, done,
+  if (launch_finish_jobs(dtype, logits, logits, V, rows, jobs, recs, part, ch.nch, rows, done,
                          out_tokens, 1, force_exact_residual(), st) != hipSuccess)
     return SV_EHIP;
   return SV_OK;
