@@ -79,7 +79,7 @@ Chunking chunking(long long rows, int V, int dt) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace layout: row-chunk partials | sampling jobs | tile records |
-// per-request counters.
+// per-request counters (and the ragged layout's validity flag after them).
 struct Carve {
   size_t part, jobs, recs, done, total;
 };
@@ -92,7 +92,7 @@ Carve carve(long long rows, int B, int V, int dt) {
   c.jobs = align256((size_t)rows * nchunk * sizeof(Partial));
   c.recs = c.jobs + align256((size_t)B * sizeof(SampleJob));
   c.done = c.recs + align256((size_t)B * ntile * sizeof(TileRec));
-  c.total = c.done + align256((size_t)B * sizeof(int));
+  c.total = c.done + align256((size_t)(B + 1) * sizeof(int));
   return c;
 }
 

@@ -37,6 +37,7 @@ struct DrawArgs {
   const void* dft;
   int V;
   int G;                 // workgroups per job
+  int B;                 // jobs
   const SampleJob* jobs; // [B]
   TileRec* recs;         // [B, ntile]
   const Partial* part;   // chunk partials (masses of skipped chunks)
@@ -60,7 +61,9 @@ __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(4))) v
   __shared__ double tab[64];                 // 2^{j/64}
   __shared__ double mass_t[64], mass_d[64];  // masses of the skipped chunks
   __shared__ int s_last;
-  const int b = blockIdx.x / A.G, g = blockIdx.x - b * A.G;
+  const JobPart jp = xcd_job_part(blockIdx.x, A.G);
+  if (jp.job >= A.B) return;  // padding of the grid to whole XCD rounds
+  const int b = jp.job, g = jp.part;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   if (tid < 64) tab[tid] = exp2_f64((double)tid * 0.015625);
   const SampleJob J = load_job(A.jobs + b, lane);
@@ -124,9 +127,9 @@ hipError_t launch_finish_jobs(int dt, const void* tgt, const void* dft, int V, i
     const int g = atoi(e);
     if (g >= 1 && g <= 64) G = g;
   }
-  if ((long long)B * G > 0x7fffffffLL) G = 1;
-  const DrawArgs A{tgt, dft, V, G, jobs, recs, part, nchunk, RT, done, out, out_width, force_exact};
-  const dim3 grid((unsigned)((long long)B * G)), blk(kNW * 64);
+  if (xcd_grid(B, G) > 0x7fffffffLL) G = 1;
+  const DrawArgs A{tgt, dft, V, G, B, jobs, recs, part, nchunk, RT, done, out, out_width, force_exact};
+  const dim3 grid((unsigned)xcd_grid(B, G)), blk(kNW * 64);
   const bool staged = tiles_per_row(V, dt) <= kPickStage;
   if (dt == 1) {
     if (staged) hipLaunchKernelGGL((k_draw_jobs<1, true>), grid, blk, 0, st, A);

@@ -27,8 +27,9 @@ __device__ __forceinline__ long long request_of_row(const Layout& L, long long r
 }
 
 // One workgroup per (row, chunk); rows are the target rows, then the draft rows.
-// The first B workgroups also zero `zero_counts` (when given), the per-request
-// counters of the chain tail kernel.
+// The first B workgroups also zero `zero_counts` (when given, B + 1 ints), the
+// per-request counters of the chain tail kernel, and workgroup 0 stores the
+// ragged layout's validity in zero_counts[B].
 template <int DT>
 __global__ __launch_bounds__(kTPB) void k_row_stats(const void* __restrict__ tgt, const void* __restrict__ dft,
                                                     int V, Layout L, const float* __restrict__ temperature,
@@ -36,20 +37,39 @@ __global__ __launch_bounds__(kTPB) void k_row_stats(const void* __restrict__ tgt
                                                     int* __restrict__ zero_counts) {
   using E = Elem<DT>;
   const long long item = blockIdx.x;
-  // per-request counters of the kernel that follows start from zero
+  // (workgroups past the last item exist for the counters only)
+  if (item < (L.RT + L.RD) * (long long)nchunk) {
+    const long long row = item / nchunk;
+    const int chunk = (int)(item - row * nchunk);
+    const bool draft = row >= L.RT;
+    const long long r = draft ? row - L.RT : row;
+    long long b = request_of_row(L, r, draft);
+    if (b < 0) b = 0;
+    if (b >= L.B) b = L.B - 1;
+    const float T = temperature[b];
+    if (temperature_ok(T) && !(draft && T == 0.0f)) {
+      const void* rowp =
+          reinterpret_cast<const char*>(draft ? dft : tgt) + (size_t)r * (size_t)V * sizeof(typename E::T);
+      row_chunk_stats<DT>(rowp, V, chunk, chunk_vecs, T, part + item);
+    }
+  }
+  // The stores for the kernel that follows come last: a store before the
+  // cu_gamma reads of request_of_row could alias them, and the compiler would
+  // then read cu_gamma through vector loads instead of the scalar cache.
+  // Per-request counters start from zero.
   if (zero_counts && item < L.B && threadIdx.x == 0) zero_counts[item] = 0;
-  if (item >= (L.RT + L.RD) * (long long)nchunk) return;  // a workgroup added for the counters only
-  const long long row = item / nchunk;
-  const int chunk = (int)(item - row * nchunk);
-  const bool draft = row >= L.RT;
-  const long long r = draft ? row - L.RT : row;
-  long long b = request_of_row(L, r, draft);
-  if (b < 0) b = 0;
-  if (b >= L.B) b = L.B - 1;
-  const float T = temperature[b];
-  if (!temperature_ok(T) || (draft && T == 0.0f)) return;
-  const void* rowp = reinterpret_cast<const char*>(draft ? dft : tgt) + (size_t)r * (size_t)V * sizeof(typename E::T);
-  row_chunk_stats<DT>(rowp, V, chunk, chunk_vecs, T, part + item);
+  // A ragged layout is checked once, here: it is usable when cu_gamma[0] == 0,
+  // it never decreases, every step is at most gamma_max and cu_gamma[B] ==
+  // total_draft (zero_counts[B] = 1 if so).
+  if (zero_counts && item == 0 && L.mode == LAYOUT_RAGGED) {
+    bool ok = threadIdx.x != 0 || (L.cu[0] == 0 && L.cu[L.B] == L.total_draft);
+    for (int k = threadIdx.x; k < L.B; k += kTPB) {
+      const int lo = L.cu[k], hi = L.cu[k + 1];
+      ok = ok && hi >= lo && hi - lo <= L.gamma;
+    }
+    ok = __syncthreads_and(ok) != 0;
+    if (threadIdx.x == 0) zero_counts[L.B] = ok ? 1 : 0;
+  }
 }
 
 hipError_t launch_row_stats(int dt, const void* tgt, const void* dft, int V, const Layout& L,

@@ -230,6 +230,26 @@ __device__ __forceinline__ T wave_reduce(T v, F op) {
   return v;
 }
 
+// Workgroups of one job on one XCD. The dispatcher hands consecutive
+// workgroup indices to the 8 XCDs of the part in turn, and each XCD has its
+// own L2; a job whose G workgroups exchange records and re-read tiles keeps
+// that traffic in one L2 when all its workgroups sit on the same XCD. Index i
+// of a grid of jobs_padded * G workgroups (jobs_padded a multiple of kXcds)
+// maps to job x + kXcds * (s / G) and part s % G, with x = i % kXcds and
+// s = i / kXcds. Only placement depends on it: any dispatch order gives the
+// same results.
+constexpr int kXcds = 8;
+struct JobPart {
+  int job, part;
+};
+__device__ __forceinline__ JobPart xcd_job_part(int i, int G) {
+  const int x = i % kXcds, s = i / kXcds;
+  return JobPart{x + kXcds * (s / G), s % G};
+}
+__host__ __device__ inline long long xcd_grid(long long jobs, int G) {
+  return (jobs + kXcds - 1) / kXcds * kXcds * G;
+}
+
 // Host-side launchers (defined next to their kernels).
 hipError_t launch_row_stats(int dt, const void* tgt, const void* dft, int V, const Layout& L,
                             const float* temperature, int chunk_vecs, int nchunk, Partial* part, int* zero_counts,

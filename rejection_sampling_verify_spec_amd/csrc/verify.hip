@@ -28,7 +28,7 @@ struct RequestArgs {
   int V;
   ChainArgs A;     // layout, per-position inputs, partials, num_accepted, diag
   TileRec* recs;   // [B, ntile]
-  int* done;       // [B] workgroups of the request finished with their tiles
+  int* done;       // [B] workgroups of the request finished with their tiles; [B]: ragged layout valid
   int32_t* out;
   int out_width;
   int ntile;       // tiles per row
@@ -48,22 +48,15 @@ __global__ __launch_bounds__(kReqWaves * 64) __attribute__((amdgpu_waves_per_eu(
   __shared__ double mass_t[64], mass_d[64];  // masses of the skipped chunks of the drawn row(s)
   __shared__ SampleJob job;
   __shared__ int s_n, s_bad, s_last;
-  const int b = blockIdx.x / R.G, g = blockIdx.x - b * R.G;
+  const JobPart jp = xcd_job_part(blockIdx.x, R.G);
+  if (jp.job >= R.A.L.B) return;  // padding of the grid to whole XCD rounds
+  const int b = jp.job, g = jp.part;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const Layout& L = R.A.L;
   if (tid < 64) tab[tid] = exp2_f64((double)tid * 0.015625);
 
-  // a ragged layout is usable when cu_gamma[0] == 0, it never decreases, every
-  // step is at most gamma_max and cu_gamma[B] == total_draft
-  bool layout_ok = true;
-  if (L.mode == LAYOUT_RAGGED) {
-    if (tid == 0) layout_ok = L.cu[0] == 0 && L.cu[L.B] == L.total_draft;
-    for (int k = tid; k < L.B; k += NT) {
-      const int lo = L.cu[k], hi = L.cu[k + 1];
-      layout_ok = layout_ok && hi >= lo && hi - lo <= L.gamma;
-    }
-    layout_ok = __syncthreads_and(layout_ok) != 0;
-  }
+  // a ragged layout's validity, checked once by the streaming kernel
+  const bool layout_ok = L.mode != LAYOUT_RAGGED || R.done[L.B] != 0;
   const ChainRows rows = layout_ok ? chain_rows(L, b) : ChainRows{0, 0, 0};
   int32_t* orow = R.out + (long long)b * R.out_width;
   accept_chain<DT, NW>(R.tgt, R.dft, R.V, R.A, b, rows, layout_ok, g == 0, orow, R.out_width, u.acc, job, mass_t,
@@ -129,7 +122,7 @@ hipError_t launch_verify_chain(int dt, const void* tgt, const void* dft, int V, 
   const long long want = (4ll * cus + L.B - 1) / L.B;
   int G = (int)(want < 4 ? 4 : (want > 8 ? 8 : want));
   G = env_int("SPECVERIFY_REQUEST_GROUPS", G, 1, 64);
-  if ((long long)L.B * G > 0x7fffffffLL) G = 1;
+  if (xcd_grid(L.B, G) > 0x7fffffffLL) G = 1;
   RequestArgs R;
   R.tgt = tgt;
   R.dft = dft;
@@ -142,7 +135,7 @@ hipError_t launch_verify_chain(int dt, const void* tgt, const void* dft, int V, 
   R.ntile = tiles_per_row(V, dt);
   R.G = G;
   R.force_exact = force_exact;
-  const dim3 grid((unsigned)((long long)L.B * G)), block(kReqWaves * 64);
+  const dim3 grid((unsigned)xcd_grid(L.B, G)), block(kReqWaves * 64);
   const bool staged = R.ntile <= kPickStage;
   if (dt == 1) {
     if (staged) hipLaunchKernelGGL((k_request<1, true>), grid, block, 0, st, R);
