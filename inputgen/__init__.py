@@ -46,11 +46,20 @@ DIST_NORMAL, DIST_T3 = 0, 1
 _lib = None
 
 
+def _compiler():
+    """gcc, or with SPECVERIFY_SANITIZE=1 ROCm's clang with AddressSanitizer and UndefinedBehaviorSanitizer
+    (the same runtime as the sanitized host code of the HIP library, so one process can load both)."""
+    if os.environ.get("SPECVERIFY_SANITIZE") == "1":
+        return ["/opt/rocm/llvm/bin/clang", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                "-fno-omit-frame-pointer", "-shared-libsan", "-g"]
+    return ["gcc"]
+
+
 def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-pthread", _SRC,
-                        "-o", tmp, "-lm"], check=True)
+        subprocess.run(_compiler() + ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-pthread", _SRC,
+                                      "-o", tmp, "-lm"], check=True)
         os.replace(tmp, _LIB)
     return _LIB
 

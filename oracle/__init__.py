@@ -27,12 +27,20 @@ MUT_TREE_NO_UPDATE, MUT_TREE_NO_RENORM = 5, 6
 _lib = None
 
 
+def _compiler():
+    """gcc, or with SPECVERIFY_SANITIZE=1 ROCm's clang with AddressSanitizer and UndefinedBehaviorSanitizer."""
+    if os.environ.get("SPECVERIFY_SANITIZE") == "1":
+        return ["/opt/rocm/llvm/bin/clang", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                "-fno-omit-frame-pointer", "-shared-libsan", "-g"]
+    return ["gcc"]
+
+
 def build(force: bool = True) -> str:
     """Compile oracle.c into liboracle.so with gcc (no fast-math, no FMA contraction)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
-               "-pthread", _SRC, "-o", tmp, "-lm"]
+        cmd = _compiler() + ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+                             "-pthread", _SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB

@@ -28,6 +28,11 @@ def build(verbose: bool = False) -> str:
            # packed fp32 instructions stay disabled on this target
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    if os.environ.get("SPECVERIFY_SANITIZE") == "1":
+        # host code only, with AddressSanitizer and UndefinedBehaviorSanitizer (device code is never built
+        # with a sanitizer); load the library with the clang ASan runtime preloaded
+        cmd += ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libsan"]
     cmd += [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
