@@ -253,10 +253,13 @@ def _timed_loop(args, sv, call, copies, pairs_per_call=1):
     import torch
     n = len(copies)
     t_warm = time.perf_counter()
-    sv.spec_verify_timing_enable(True)
+    events = not args.no_kernel_events
+    if events:
+        sv.spec_verify_timing_enable(True)
     for i in range(max(args.warmup, 1)):
         call(copies[i % n])
-    sv.spec_verify_timing_enable(False)
+    if events:
+        sv.spec_verify_timing_enable(False)
     torch.cuda.synchronize()
     sv.spec_verify_timing_reset()
     # settle: more untimed calls until args.settle_ms of wall time have passed since the warm-up
@@ -290,14 +293,16 @@ def _timed_loop(args, sv, call, copies, pairs_per_call=1):
     torch.cuda.synchronize()
     step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(nd)]
 
-    nk = max(20, min(args.steps, 200))
-    sv.spec_verify_timing_enable(True)
-    for i in range(nk):
-        call(copies[i % n])
-    sv.spec_verify_timing_enable(False)
-    torch.cuda.synchronize()
-    k_ms = sv.spec_verify_timing_read(nk * pairs_per_call)
-    sv.spec_verify_timing_reset()
+    k_ms = []
+    if events:
+        nk = max(20, min(args.steps, 200))
+        sv.spec_verify_timing_enable(True)
+        for i in range(nk):
+            call(copies[i % n])
+        sv.spec_verify_timing_enable(False)
+        torch.cuda.synchronize()
+        k_ms = sv.spec_verify_timing_read(nk * pairs_per_call)
+        sv.spec_verify_timing_reset()
     return {"elapsed": elapsed, "gpu_ms": gpu_ms, "step_ms": step_ms, "k_ms": k_ms, "outs": outs,
             "settle_calls": settle}
 
@@ -817,6 +822,8 @@ def main():
     ap.add_argument("--cpu1-seconds", type=float, default=4.0,
                     help="wall time spent timing the CPU oracle on one thread")
     ap.add_argument("--skip-cpu-baseline", action="store_true", help="no oracle run (profiling runs)")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="do not create the library's kernel events (profiling runs: the profiler times the kernels)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pooled-parity", metavar="NAMES",
                     help="comma-separated workloads (tiny,mid,large,ragged): GPU against the oracle over many seeds")
