@@ -238,12 +238,14 @@ __device__ __forceinline__ void write_skipped_rec(TileRec* rec, bool head, doubl
 // a and k/64 are within a factor of two of each other or r is the tiny rest),
 // and 2^r = exp(r ln 2) by its Taylor series to degree 5 (truncation below
 // 4e-17 relative). About 3 ulp in all.
-// p * r + c as the three-operand v_fma_f64: the compiler otherwise picks the
-// accumulating form, which overwrites its addend and so copies the constant
-// coefficient into a fresh register before every step.
+// p * r + c as the three-operand v_fma_f64 with the constant coefficient c in
+// a scalar register pair (one scalar operand per instruction): the compiler
+// otherwise picks the accumulating form, which overwrites its addend and so
+// copies the coefficient into fresh vector registers before every step, or
+// keeps every coefficient in vector registers across the tile loops.
 __device__ __forceinline__ double fma3_f64(double p, double r, double c) {
   double d;
-  __asm__("v_fma_f64 %0, %1, %2, %3" : "=v"(d) : "v"(p), "v"(r), "v"(c));
+  __asm__("v_fma_f64 %0, %1, %2, %3" : "=v"(d) : "v"(p), "v"(r), "s"(c));
   return d;
 }
 
@@ -260,17 +262,13 @@ __device__ __forceinline__ double exp2_tab(double a, const double* tab) {
   return __builtin_ldexp(tab[ki & 63] * p, ki >> 6);
 }
 
-// Mass 2^{(l - m) c} of one token in double precision (c64 = c, c32 = fl32(c)),
-// in units of its row's maximum. Terms below 2^-50 of the row maximum (fp32
-// argument a32 < kTinyExp) take the fp32 exponential unit: the argument's error
-// (three fp32 roundings, about 2e-7 |a|) and the unit's ulp leave an absolute
-// error below 2^-60 per token, under the rounding of the double-precision sums
-// these terms enter.
-__device__ __forceinline__ double emass_t(float l, float m, double c64, float c32, const double* tab) {
-  const float a32 = (l - m) * c32;
-  if (a32 < kTinyExp) return (double)exp2_f32(a32);  // also l = -inf
-  // here a >= kTinyExp less a relative 1e-6: inside exp2_tab's range
-  return exp2_tab(((double)l - (double)m) * c64, tab);
+// Mass 2^{(l - m) c} of one token in double precision (c64 = c), in units of
+// its row's maximum. Arguments below -1100 (masses that are 0 in fp64, and
+// l = -inf) are raised to -1100, inside exp2_tab's range; NaN propagates.
+// Selects rather than a branch: every lane takes the same instructions.
+__device__ __forceinline__ double emass_t(float l, float m, double c64, const double* tab) {
+  const double a = ((double)l - (double)m) * c64;
+  return exp2_tab(a < -1100.0 ? -1100.0 : a, tab);
 }
 
 // ---------------------------------------------------------------------------
@@ -674,10 +672,10 @@ __device__ __forceinline__ void exact_token(bool has, float xt, float xd, const 
   double et = 0.0, ed = 0.0;
   bool und = false;
   if (has) {
-    et = emass_t(xt, J.mt, J.c64, J.c32, tab);
+    et = emass_t(xt, J.mt, J.c64, tab);
     A.zt += et;
     if (RES) {
-      ed = emass_t(xd, J.md, J.c64, J.c32, tab);
+      ed = emass_t(xd, J.md, J.c64, tab);
       A.zd += ed;
       if (et > hi * ed) {
         A.dp += et - J.rho * ed;
@@ -1106,7 +1104,7 @@ __device__ __forceinline__ void pick_impl(const char* trow, const char* drow, in
       double acc = 0.0;
 #pragma unroll
       for (int i = 0; i < bt; ++i) {
-        const double q = emass_t(xt[i], J.mt, J.c64, J.c32, tab) - rho * emass_t(xd[i], J.md, J.c64, J.c32, tab);
+        const double q = emass_t(xt[i], J.mt, J.c64, tab) - rho * emass_t(xd[i], J.md, J.c64, tab);
         acc += q > 0.0 ? q : 0.0;
       }
       acc = block_sum<NW>(acc, P.red);
@@ -1149,9 +1147,9 @@ __device__ __forceinline__ void pick_impl(const char* trow, const char* drow, in
       if (res) load_tile_block<DT, NW>(drow, t * tok, V, xd);
 #pragma unroll
       for (int i = 0; i < bt; ++i) {
-        double v = emass_t(xt[i], J.mt, J.c64, J.c32, tab);
+        double v = emass_t(xt[i], J.mt, J.c64, tab);
         if (res) {
-          v -= rho * emass_t(xd[i], J.md, J.c64, J.c32, tab);
+          v -= rho * emass_t(xd[i], J.md, J.c64, tab);
           v = v > 0.0 ? v : 0.0;
         }
         q[i] = v;

@@ -122,7 +122,7 @@ __device__ __forceinline__ double sum_segments(const double* buf, int nseg, int 
 // lanes (result in P.flag).
 template <int DT>
 __device__ __forceinline__ void child_test(const LLArgs& A, LLSpace& P, long long t0, long long d0, int v, int nrej,
-                                           int c, double c64, float c32) {
+                                           int c, double c64) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int x = P.tok[c];
   if (tid < 64) {
@@ -132,11 +132,11 @@ __device__ __forceinline__ void child_test(const LLArgs& A, LLSpace& P, long lon
       double m = 0.0;
       if (l == 0) {
         const float lt = Elem<DT>::at(A.tgt, (t0 + v) * (long long)A.V + x);
-        m = emass_t(lt, P.mt[v], c64, c32, P.tab) * (1.0 / P.zt[v]);
+        m = emass_t(lt, P.mt[v], c64, P.tab) * (1.0 / P.zt[v]);
       } else if (l < nrej + 2) {
         const int w = l <= nrej ? P.rej[l - 1] : c;
         const float ld = Elem<DT>::at(A.dft, (d0 + w - 1) * (long long)A.V + x);
-        m = emass_t(ld, P.md[w], c64, c32, P.tab) * (1.0 / P.zd[w]);
+        m = emass_t(ld, P.md[w], c64, P.tab) * (1.0 / P.zd[w]);
       }
       const int n = min(64, nrej + 2 - l0);
       for (int k = 0; k < n; ++k) {
@@ -174,7 +174,7 @@ constexpr int kSegBatch = 2;  // segments of one wave whose loads are in flight 
 template <int DT>
 __device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P, const char* trow, long long d0,
                                               int v, int nrej, const int (&seg)[kSegBatch], int lane, double c64,
-                                              float c32, double (&R)[kSegBatch * Elem<DT>::kPerVec]) {
+                                              double (&R)[kSegBatch * Elem<DT>::kPerVec]) {
   constexpr int epv = Elem<DT>::kPerVec;
   constexpr int es = sizeof(typename Elem<DT>::T);
   auto drow = [&](int k) {
@@ -199,7 +199,7 @@ __device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P,
       float x[epv];
       unpack<DT>(w[i], x);
 #pragma unroll
-      for (int e = 0; e < epv; ++e) R[i * epv + e] = emass_t(x[e], mt, c64, c32, P.tab) * izt;
+      for (int e = 0; e < epv; ++e) R[i * epv + e] = emass_t(x[e], mt, c64, P.tab) * izt;
     }
   }
   while (k < nrej) {
@@ -219,7 +219,7 @@ __device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P,
       float x[epv];
       unpack<DT>(w[i], x);
 #pragma unroll
-      for (int e = 0; e < epv; ++e) R[i * epv + e] = residual_step(R[i * epv + e], s, emass_t(x[e], md, c64, c32, P.tab));
+      for (int e = 0; e < epv; ++e) R[i * epv + e] = residual_step(R[i * epv + e], s, emass_t(x[e], md, c64, P.tab));
     }
     k = k2;
   }
@@ -230,7 +230,7 @@ __device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P,
 // of R; then the team meets. Returns false when the wait ran out of polls.
 template <int DT>
 __device__ bool team_pass(const LLArgs& A, LLSpace& P, long long t0, long long d0, int v, int nrej, double* buf,
-                          int* ctr, int target, int rank, double c64, float c32) {
+                          int* ctr, int target, int rank, double c64) {
   constexpr int epv = Elem<DT>::kPerVec;
   constexpr int es = sizeof(typename Elem<DT>::T);
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
@@ -241,7 +241,7 @@ __device__ bool team_pass(const LLArgs& A, LLSpace& P, long long t0, long long d
 #pragma unroll
     for (int i = 0; i < kSegBatch; ++i) seg[i] = s0 + i * nw < A.nseg ? s0 + i * nw : -1;
     double R[kSegBatch * epv];
-    residual_segs<DT>(A, P, trow, d0, v, nrej, seg, lane, c64, c32, R);
+    residual_segs<DT>(A, P, trow, d0, v, nrej, seg, lane, c64, R);
 #pragma unroll
     for (int i = 0; i < kSegBatch; ++i) {
       double s = 0.0;
@@ -298,7 +298,7 @@ __device__ __forceinline__ void list_children(LLSpace& P, int N, int v) {
 // in it; the last token of positive mass when rounding leaves none.
 template <int DT>
 __device__ int pick_token(const LLArgs& A, LLSpace& P, long long t0, long long d0, int v, int nrej,
-                          const double* buf, double thr, double c64, float c32, int lane) {
+                          const double* buf, double thr, double c64, int lane) {
   constexpr int epv = Elem<DT>::kPerVec;
   // the segment
   double base = 0.0;
@@ -335,7 +335,7 @@ __device__ int pick_token(const LLArgs& A, LLSpace& P, long long t0, long long d
 #pragma unroll
   for (int i = 1; i < kSegBatch; ++i) seg[i] = -1;
   double R[kSegBatch * epv];
-  residual_segs<DT>(A, P, trow, d0, v, nrej, seg, lane, c64, c32, R);
+  residual_segs<DT>(A, P, trow, d0, v, nrej, seg, lane, c64, R);
   const int jl = (sg * 64 + lane) * epv;
   double s = 0.0;
 #pragma unroll
@@ -479,7 +479,7 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
       int accepted = -1;
       for (int i = 0; i < P.nk; ++i) {
         const int c = P.kids[i];
-        child_test<DT>(A, P, t0, d0, v, nrej, c, c64, c32);
+        child_test<DT>(A, P, t0, d0, v, nrej, c, c64);
         if (P.flag) {
           accepted = c;
           break;
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
         ++nrej;
         ++passes;
         if (!team_pass<DT>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr, passes * A.G, rank,
-                           c64, c32)) {
+                           c64)) {
           failed = true;
           break;
         }
@@ -518,7 +518,7 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
     if (!failed && !have_sums) {
       ++passes;
       failed = !team_pass<DT>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr, passes * A.G,
-                              rank, c64, c32);
+                              rank, c64);
     }
     if (failed) {
       // a team wait ran out of polls: this team's remaining requests report -1
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
       const double* buf = sums + (size_t)(passes & 1) * A.nseg;
       const double S = sum_segments(buf, A.nseg, lane);
       const double thr = (double)A.us[t0 + v] * S;
-      const int y = pick_token<DT>(A, P, t0, d0, v, nrej, buf, thr, c64, c32, lane);
+      const int y = pick_token<DT>(A, P, t0, d0, v, nrej, buf, thr, c64, lane);
       if (lane == 0) {
         orow[d] = y;
         A.num_acc[b] = d;
