@@ -763,17 +763,28 @@ __device__ __forceinline__ void tile_pass(uint4 (&wt)[4], uint4 (&wd)[4], const 
   // unpacked further).
   const float tt = mt + kDropExp / c32, td = RES ? md + kDropExp / c32 : 0.f;
   uint32_t live = 0u;
+  // vectors u whose every token, in every lane, lies at or above 2^kTinyExp of
+  // its row maximum in the target row (or the draft row of a residual): the
+  // triage would flag each of them and add +0 to every sum, so it skips them.
+  // (x - m) * c is monotone in x in fp32 as in exact arithmetic, so the test on
+  // the vector's smallest logit is the triage's own test on every token.
+  uint32_t dense = 0u;  // wave-uniform, bit u
 #pragma unroll
   for (int u = 0; u < nv; ++u) {
     float xt[epv], xd[epv];
     unpack<DT>(wt[u], xt);
     if (RES) unpack<DT>(wd[u], xd);
-    float vt = xt[0], vd = RES ? xd[0] : 0.f;
+    float vt = xt[0], vd = RES ? xd[0] : 0.f, nt = xt[0], nd = RES ? xd[0] : 0.f;
 #pragma unroll
     for (int e = 1; e < epv; ++e) {
       vt = fmaxf(vt, xt[e]);
-      if (RES) vd = fmaxf(vd, xd[e]);
+      nt = fminf(nt, xt[e]);
+      if (RES) {
+        vd = fmaxf(vd, xd[e]);
+        nd = fminf(nd, xd[e]);
+      }
     }
+    if (__all((nt - mt) * c32 >= kTinyExp) || (RES && __all((nd - md) * c32 >= kTinyExp))) dense |= 1u << u;
     if (!__any(vt >= tt || (RES && vd >= td))) continue;
 #pragma unroll
     for (int e = 0; e < epv; ++e) {
@@ -825,6 +836,10 @@ __device__ __forceinline__ void tile_pass(uint4 (&wt)[4], uint4 (&wd)[4], const 
     // fp32 triage of every token of the live vectors
 #pragma unroll
     for (int u = 0; u < nv; ++u) {
+      if ((dense >> u) & 1u) {
+        flags |= ((1u << epv) - 1u) << (u * epv);
+        continue;
+      }
       if (!__any(((live >> (u * epv)) & ((1u << epv) - 1u)) != 0u)) continue;
       // unpacked again rather than kept from the mask pass (register pressure)
       uint4 t4 = wt[u], d4 = RES ? wd[u] : wt[u];
