@@ -248,13 +248,24 @@ __device__ __forceinline__ double fma3_f64(double p, double r, double c) {
   __asm__("v_fma_f64 %0, %1, %2, %3" : "=v"(d) : "v"(p), "v"(r), "s"(c));
   return d;
 }
+// The first step, c1 * r + c0, with c1 in a scalar and c0 in a vector register
+// pair (both constants; a scalar pair for each would exceed the one scalar
+// operand an instruction may read).
+__device__ __forceinline__ double fma_first_f64(double r, double c1, double c0) {
+  double d;
+  __asm__("v_fma_f64 %0, %1, %2, %3" : "=v"(d) : "v"(r), "s"(c1), "v"(c0));
+  return d;
+}
 
 __device__ __forceinline__ double exp2_tab(double a, const double* tab) {
-  const double k = __builtin_rint(a * 64.0);
+  // k = rint(64 a) by the shifter 1.5 * 2^52 (|64 a| < 2^51): the low 32 bits
+  // of t hold k as a two's-complement int
+  double t;
+  __asm__("v_fma_f64 %0, %1, %2, %3" : "=v"(t) : "v"(a), "s"(64.0), "v"(0x1.8p52));
+  const double k = t - 0x1.8p52;
   const double r = __builtin_fma(k, -0.015625, a);
-  const int ki = (int)k;
-  double p = 0x1.5d87fe78a6731p-10;  // ln2^5 / 5!
-  p = fma3_f64(p, r, 0x1.3b2ab6fba4e77p-7);  // ln2^4 / 4!
+  const int ki = (int)(uint32_t)(uint64_t)__double_as_longlong(t);
+  double p = fma_first_f64(r, 0x1.5d87fe78a6731p-10, 0x1.3b2ab6fba4e77p-7);  // ln2^5 / 5!, ln2^4 / 4!
   p = fma3_f64(p, r, 0x1.c6b08d704a0c0p-5);  // ln2^3 / 3!
   p = fma3_f64(p, r, 0x1.ebfbdff82c58fp-3);  // ln2^2 / 2!
   p = fma3_f64(p, r, 0x1.62e42fefa39efp-1);  // ln2
@@ -264,11 +275,12 @@ __device__ __forceinline__ double exp2_tab(double a, const double* tab) {
 
 // Mass 2^{(l - m) c} of one token in double precision (c64 = c), in units of
 // its row's maximum. Arguments below -1100 (masses that are 0 in fp64, and
-// l = -inf) are raised to -1100, inside exp2_tab's range; NaN propagates.
-// Selects rather than a branch: every lane takes the same instructions.
+// l = -inf) are raised to -1100, inside exp2_tab's range, by one max rather
+// than a branch. A NaN argument would also give 0, but no draw reads a row
+// with a NaN or +inf logit: the streaming pass flags such rows and their
+// requests fail before any draw.
 __device__ __forceinline__ double emass_t(float l, float m, double c64, const double* tab) {
-  const double a = ((double)l - (double)m) * c64;
-  return exp2_tab(a < -1100.0 ? -1100.0 : a, tab);
+  return exp2_tab(fmax(((double)l - (double)m) * c64, -1100.0), tab);
 }
 
 // ---------------------------------------------------------------------------
