@@ -257,20 +257,35 @@ __device__ __forceinline__ double fma_first_f64(double r, double c1, double c0) 
   return d;
 }
 
-__device__ __forceinline__ double exp2_tab(double a, const double* tab) {
+// The two constants exp2_tab reads from vector registers (the shifter and the
+// degree-4 coefficient). Built by pinned_exp2() before a loop, they are opaque
+// to the compiler, which otherwise rebuilds them for every token.
+struct Exp2Regs {
+  double shift, c4;
+};
+__device__ __forceinline__ Exp2Regs pinned_exp2() {
+  Exp2Regs K{0x1.8p52, 0x1.3b2ab6fba4e77p-7};
+  __asm__ volatile("" : "+v"(K.shift), "+v"(K.c4));
+  return K;
+}
+
+__device__ __forceinline__ double exp2_tab(double a, const double* tab, const Exp2Regs& K) {
   // k = rint(64 a) by the shifter 1.5 * 2^52 (|64 a| < 2^51): the low 32 bits
   // of t hold k as a two's-complement int
   double t;
-  __asm__("v_fma_f64 %0, %1, %2, %3" : "=v"(t) : "v"(a), "s"(64.0), "v"(0x1.8p52));
+  __asm__("v_fma_f64 %0, %1, %2, %3" : "=v"(t) : "v"(a), "s"(64.0), "v"(K.shift));
   const double k = t - 0x1.8p52;
   const double r = __builtin_fma(k, -0.015625, a);
   const int ki = (int)(uint32_t)(uint64_t)__double_as_longlong(t);
-  double p = fma_first_f64(r, 0x1.5d87fe78a6731p-10, 0x1.3b2ab6fba4e77p-7);  // ln2^5 / 5!, ln2^4 / 4!
+  double p = fma_first_f64(r, 0x1.5d87fe78a6731p-10, K.c4);  // ln2^5 / 5!, ln2^4 / 4!
   p = fma3_f64(p, r, 0x1.c6b08d704a0c0p-5);  // ln2^3 / 3!
   p = fma3_f64(p, r, 0x1.ebfbdff82c58fp-3);  // ln2^2 / 2!
   p = fma3_f64(p, r, 0x1.62e42fefa39efp-1);  // ln2
   p = __builtin_fma(p, r, 1.0);
   return __builtin_ldexp(tab[ki & 63] * p, ki >> 6);
+}
+__device__ __forceinline__ double exp2_tab(double a, const double* tab) {
+  return exp2_tab(a, tab, Exp2Regs{0x1.8p52, 0x1.3b2ab6fba4e77p-7});
 }
 
 // Mass 2^{(l - m) c} of one token in double precision (c64 = c), in units of
@@ -279,6 +294,9 @@ __device__ __forceinline__ double exp2_tab(double a, const double* tab) {
 // than a branch. A NaN argument would also give 0, but no draw reads a row
 // with a NaN or +inf logit: the streaming pass flags such rows and their
 // requests fail before any draw.
+__device__ __forceinline__ double emass_t(float l, float m, double c64, const double* tab, const Exp2Regs& K) {
+  return exp2_tab(fmax(((double)l - (double)m) * c64, -1100.0), tab, K);
+}
 __device__ __forceinline__ double emass_t(float l, float m, double c64, const double* tab) {
   return exp2_tab(fmax(((double)l - (double)m) * c64, -1100.0), tab);
 }
@@ -680,14 +698,14 @@ struct ExactAcc {
 template <bool RES, int NW>
 __device__ __forceinline__ void exact_token(bool has, float xt, float xd, const SampleJob& J, double hi, double lo,
                                             unsigned long long below, ExactAcc& A, TileLists<NW>& L, int wv,
-                                            const double* tab) {
+                                            const double* tab, const Exp2Regs& K) {
   double et = 0.0, ed = 0.0;
   bool und = false;
   if (has) {
-    et = emass_t(xt, J.mt, J.c64, tab);
+    et = emass_t(xt, J.mt, J.c64, tab, K);
     A.zt += et;
     if (RES) {
-      ed = emass_t(xd, J.md, J.c64, tab);
+      ed = emass_t(xd, J.md, J.c64, tab, K);
       A.zd += ed;
       if (et > hi * ed) {
         A.dp += et - J.rho * ed;
@@ -878,6 +896,7 @@ __device__ __forceinline__ void tile_pass(uint4 (&wt)[4], uint4 (&wd)[4], const 
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     __builtin_amdgcn_wave_barrier();
   }
+  const Exp2Regs K = pinned_exp2();
   if (all_flagged) {
     // every token of the tile is flagged (rows with mass everywhere): the
     // double-precision pass runs straight through the staged vectors, token i
@@ -891,7 +910,7 @@ __device__ __forceinline__ void tile_pass(uint4 (&wt)[4], uint4 (&wd)[4], const 
       if (RES) unpack<DT>(G.d[wv][u][lane], xd);
 #pragma unroll
       for (int e = 0; e < epv; ++e)
-        exact_token<RES, NW>(true, xt[e], RES ? xd[e] : 0.f, J, hi, lo, below, A, L, wv, tab);
+        exact_token<RES, NW>(true, xt[e], RES ? xd[e] : 0.f, J, hi, lo, below, A, L, wv, tab, K);
     }
     __builtin_amdgcn_wave_barrier();
   } else if (any_flagged) {
@@ -907,7 +926,7 @@ __device__ __forceinline__ void tile_pass(uint4 (&wt)[4], uint4 (&wd)[4], const 
         xt = staged_at<DT>(G.t[wv][i / epv][lane], i % epv);
         if (RES) xd = staged_at<DT>(G.d[wv][i / epv][lane], i % epv);
       }
-      exact_token<RES, NW>(has, xt, xd, J, hi, lo, below, A, L, wv, tab);
+      exact_token<RES, NW>(has, xt, xd, J, hi, lo, below, A, L, wv, tab, K);
     }
     // the stage and the lists are reused by the wave's next tile
     __builtin_amdgcn_wave_barrier();
@@ -1123,6 +1142,7 @@ __device__ __forceinline__ void pick_impl(const char* trow, const char* drow, in
   // kRecRecomputed, mass in zd), and the scan
   if (P.any_exact) {
     const bool all = P.any_exact == 2;
+    const Exp2Regs K = pinned_exp2();
     for (int k = 0; k < ntile; ++k) {
       if (!(all || rng(k) == kRecOverflow)) continue;
       float xt[bt], xd[bt];
@@ -1131,7 +1151,7 @@ __device__ __forceinline__ void pick_impl(const char* trow, const char* drow, in
       double acc = 0.0;
 #pragma unroll
       for (int i = 0; i < bt; ++i) {
-        const double q = emass_t(xt[i], J.mt, J.c64, tab) - rho * emass_t(xd[i], J.md, J.c64, tab);
+        const double q = emass_t(xt[i], J.mt, J.c64, tab, K) - rho * emass_t(xd[i], J.md, J.c64, tab, K);
         acc += q > 0.0 ? q : 0.0;
       }
       acc = block_sum<NW>(acc, P.red);
@@ -1165,6 +1185,7 @@ __device__ __forceinline__ void pick_impl(const char* trow, const char* drow, in
   if (!res && rng(tile) == kRecChunkHead) tile_end = min(ntile, tile + J.chunk_tiles);
   double base = Wtile;
   int found = 0x7fffffff, lastpos = -1;
+  const Exp2Regs K = pinned_exp2();
   for (int t = tile; t < tile_end; ++t) {
     double q[bt];
     double local = 0.0;
@@ -1174,9 +1195,9 @@ __device__ __forceinline__ void pick_impl(const char* trow, const char* drow, in
       if (res) load_tile_block<DT, NW>(drow, t * tok, V, xd);
 #pragma unroll
       for (int i = 0; i < bt; ++i) {
-        double v = emass_t(xt[i], J.mt, J.c64, tab);
+        double v = emass_t(xt[i], J.mt, J.c64, tab, K);
         if (res) {
-          v -= rho * emass_t(xd[i], J.md, J.c64, tab);
+          v -= rho * emass_t(xd[i], J.md, J.c64, tab, K);
           v = v > 0.0 ? v : 0.0;
         }
         q[i] = v;

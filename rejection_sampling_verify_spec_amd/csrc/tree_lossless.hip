@@ -191,6 +191,7 @@ __device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P,
 #pragma unroll
     for (int i = 0; i < kSegBatch; ++i) wn[i] = load_vec<DT>(dr, tokj(i), A.V);
   }
+  const Exp2Regs K = pinned_exp2();
   {
     const float mt = P.mt[v];
     const double izt = 1.0 / P.zt[v];
@@ -199,7 +200,7 @@ __device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P,
       float x[epv];
       unpack<DT>(w[i], x);
 #pragma unroll
-      for (int e = 0; e < epv; ++e) R[i * epv + e] = emass_t(x[e], mt, c64, P.tab) * izt;
+      for (int e = 0; e < epv; ++e) R[i * epv + e] = emass_t(x[e], mt, c64, P.tab, K) * izt;
     }
   }
   while (k < nrej) {
@@ -219,7 +220,7 @@ __device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P,
       float x[epv];
       unpack<DT>(w[i], x);
 #pragma unroll
-      for (int e = 0; e < epv; ++e) R[i * epv + e] = residual_step(R[i * epv + e], s, emass_t(x[e], md, c64, P.tab));
+      for (int e = 0; e < epv; ++e) R[i * epv + e] = residual_step(R[i * epv + e], s, emass_t(x[e], md, c64, P.tab, K));
     }
     k = k2;
   }
