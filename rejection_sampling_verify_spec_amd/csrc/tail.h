@@ -884,8 +884,16 @@ __device__ __forceinline__ void tile_pass(uint4 (&wt)[4], uint4 (&wd)[4], const 
     }
   }
   ExactAcc A{(double)st, (double)sd, (double)sdp, (double)sbp, 0};
-  constexpr uint32_t kAll = nv * epv == 32 ? 0xffffffffu : ((1u << (nv * epv)) - 1u);
-  const bool all_flagged = __all(flags == kAll);
+  // Nearly every token flagged (the busiest lane has at least 3/4 of its tokens
+  // flagged; the flagged loop takes as many steps as that lane, each dearer than
+  // a step of the straight pass): every token of the tile takes the straight
+  // double-precision pass. The fp32 sums of the few unflagged tokens are then
+  // dropped: double precision only makes their masses more accurate, and it
+  // puts each on the side of the band its fp32 triage did (that side was clear
+  // by twice the band).
+  const int busiest = wave_minmax<true>(__builtin_popcount(flags));
+  const bool all_flagged = busiest * 4 >= nv * epv * 3;
+  if (all_flagged) A = ExactAcc{0.0, 0.0, 0.0, 0.0, 0};
   const bool any_flagged = __any(flags != 0u);
   if (any_flagged) {  // the fixups read the tile from an LDS copy
 #pragma unroll
@@ -898,9 +906,10 @@ __device__ __forceinline__ void tile_pass(uint4 (&wt)[4], uint4 (&wd)[4], const 
   }
   const Exp2Regs K = pinned_exp2();
   if (all_flagged) {
-    // every token of the tile is flagged (rows with mass everywhere): the
-    // double-precision pass runs straight through the staged vectors, token i
-    // of every lane at step i -- the order of the flagged loop below
+    // (nearly) every token of the tile is flagged (rows with mass everywhere):
+    // the double-precision pass runs straight through the staged vectors,
+    // token i of every lane at step i -- the order of the flagged loop below
+    // when every token is flagged
     const double hi = J.rho * (1.0 + kRhoBand), lo = J.rho * (1.0 - kRhoBand);
     const unsigned long long below = (1ull << lane) - 1ull;
 #pragma unroll 1
