@@ -645,8 +645,20 @@ def run_bench(args):
 
 # Pooled parity: seeds 1000 + k of a workload until at least 10^4 requests (the near-tie rate of
 # the parity bar is a fraction of requests, so it needs that many to be measured at all)
-POOL_SEEDS = {"tiny": 1250, "mid": 157, "large": 40, "ragged": 10}
+POOL_SEEDS = {"tiny": 1250, "mid": 157, "large": 40, "ragged": 10, "tree_near": 40}
 FLAG = 1e-5
+# tree_near: lossless multi-candidate trees with near-identical drafts and forced rejections, 250
+# trees of V=30000 per seed; seed k takes case k % 4 (dtype, noise of the draft rows)
+NEAR_CASES = (("f32", 0.003), ("f32", 0.01), ("f32", 0.03), ("bf16", 0.05))
+
+
+def pooled_inputs(name, seed):
+    """The inputs of one pooled seed and the workload whose call and oracle they take."""
+    import inputgen
+    if name == "tree_near":
+        dtype, noise = NEAR_CASES[(seed - 1000) % len(NEAR_CASES)]
+        return inputgen.near_identical_trees(250, 30000, seed, dtype=dtype, noise_sd=noise), "tree_lossless"
+    return inputgen.make(name, seed=seed), name
 
 
 def run_pooled(args):
@@ -656,7 +668,6 @@ def run_pooled(args):
     with the counts and rates per workload."""
     import torch
 
-    import inputgen
     import rejection_sampling_verify_spec_amd as sv
     dev = torch.device("cuda:0")
     names = [n for n in args.pooled_parity.split(",") if n]
@@ -668,12 +679,12 @@ def run_pooled(args):
                  fallback_requests=0, error_requests=0)
         t0 = time.time()
         for k in range(seeds):
-            d = inputgen.make(name, seed=1000 + k)
+            d, kind = pooled_inputs(name, 1000 + k)
             t = device_inputs(d, dev)
-            outs = make_call(sv, name, t, d)(t)
+            outs = make_call(sv, kind, t, d)(t)
             torch.cuda.synchronize()
             out, na = outs[0].cpu().numpy(), outs[-1].cpu().numpy()
-            ref = oracle_call(name, d, host_cores())
+            ref = oracle_call(kind, d, host_cores())
             mism = (na != ref["num_accepted"]) | (out != ref["out_tokens"]).any(axis=1)
             flagged = (ref["acc_margin"] < FLAG) | (ref["cdf_margin"] < FLAG)
             c["requests"] += int(na.shape[0])
@@ -826,7 +837,8 @@ def main():
                     help="do not create the library's kernel events (profiling runs: the profiler times the kernels)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pooled-parity", metavar="NAMES",
-                    help="comma-separated workloads (tiny,mid,large,ragged): GPU against the oracle over many seeds")
+                    help="comma-separated workloads (tiny,mid,large,ragged,tree_near): GPU against the oracle over many "
+                         "seeds")
     ap.add_argument("--pool-seeds", type=int, default=None, help="seeds per workload for --pooled-parity")
     ap.add_argument("--summarize-rocprof", metavar="DIR")
     ap.add_argument("--write-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),

@@ -314,6 +314,24 @@ def tree_inputs(B, V, seed, *, n_nodes=64, fanout=(4, 4, 3), dtype="bf16", scale
     )
 
 
+def near_identical_trees(B, V, seed, *, dtype, noise_sd):
+    """Token trees (21 nodes: 4 children of the root, 4 under each, one under each of those) whose
+    draft rows lie within noise_sd of their parent's target row, T = 1. The first child of every
+    node, and every second sibling after it, gets an acceptance uniform of 0.999, so most of them
+    are rejected and the residual they leave (about the rows' total variation) is small."""
+    d = tree_inputs(B, V, seed, n_nodes=21, fanout=(4, 4, 1), dtype=dtype, noise_sd=noise_sd)
+    ua = d["u_accept"].copy()
+    par = d["parents"]
+    for b in range(par.shape[0]):
+        for v in range(1, par.shape[1]):
+            p = int(par[b, v])
+            first = min(c for c in range(1, par.shape[1]) if par[b, c] == p)
+            if v == first or (v - first) % 2 == 1:
+                ua[b, v] = 0.999
+    d["u_accept"] = ua
+    return d
+
+
 WORKLOADS = {
     "tiny": dict(kind="chain", B=8, gamma=4, V=256, dtype="f32", scale=2.0, noise_sd=0.7, temperature=1.0,
                  seed=1),

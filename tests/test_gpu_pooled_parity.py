@@ -2,9 +2,9 @@
 over requests, so it needs at least 10^4 requests to be measured. Every request where the GPU and
 the oracle differ must be flagged by the oracle (a uniform within 1e-5 of its acceptance ratio, or
 u*S within 1e-5*S of a CDF boundary), and differing requests must stay below 1e-4 of all requests.
-Tiny and mid pool 10^4 requests here; the large workload pools 2048 here (its inputs take seconds
-per seed to generate) and ``bench.py --pooled-parity tiny,mid,large,ragged`` runs every workload at
-10^4 or more."""
+Tiny and mid pool 10^4 requests here; the large workload pools 2048 and the near-identical lossless
+trees 2000 here (their inputs take seconds per seed to generate), and ``bench.py --pooled-parity
+tiny,mid,large,ragged,tree_near`` runs every case at 10^4 or more."""
 import numpy as np
 import pytest
 
@@ -50,3 +50,35 @@ def test_pooled(sv, name, seeds):
     assert unflagged == 0
     assert mism < 1e-4 * req
     assert (np.asarray(req) >= (10_000 if name != "large" else 2048))
+
+
+def test_pooled_near_identical_lossless_trees(sv):
+    """Lossless multi-candidate trees whose drafts lie within a small noise of their parents'
+    target rows, with forced rejections (the residual a rejected sibling leaves is then about the
+    rows' total variation): 8 seeds of 250 trees, 2000 trees over four draft-noise cases.
+    ``bench.py --pooled-parity tree_near`` runs 10^4."""
+    import torch
+    cases = (("f32", 0.003), ("f32", 0.01), ("f32", 0.03), ("bf16", 0.05))
+    req = mism = unflagged = flagged = 0
+    for k in range(8):
+        dtype, noise = cases[k % 4]
+        d = inputgen.near_identical_trees(250, 30000, 1000 + k, dtype=dtype, noise_sd=noise)
+        t = device_inputs(d)
+        out, nodes, na = sv.verify_tree_lossless(t["target"], t["draft"], t["node_tokens"], t["parents"],
+                                                 t["u_accept"], t["u_sample"], t["temperature"], d["max_depth"])
+        torch.cuda.synchronize()
+        out, na = out.cpu().numpy(), na.cpu().numpy()
+        ref = oracle.verify_tree_lossless(d["target"], d["draft"], d["node_tokens"], d["parents"], d["u_accept"],
+                                          d["u_sample"], d["temperature"], d["max_depth"])
+        m = (na != ref["num_accepted"]) | (out != ref["out_tokens"]).any(axis=1)
+        f = (ref["acc_margin"] < FLAG) | (ref["cdf_margin"] < FLAG)
+        req += na.shape[0]
+        mism += int(m.sum())
+        unflagged += int((m & ~f).sum())
+        flagged += int(f.sum())
+        print(f"[pooled near-identical trees] seed {1000 + k} {dtype} sd={noise}: {req} trees, {mism} mismatches",
+              flush=True)
+    print(f"[pooled near-identical trees] {req} trees, {mism} mismatches ({unflagged} unflagged), "
+          f"flagged {flagged / req:.4f}", flush=True)
+    assert unflagged == 0
+    assert mism <= 1e-4 * req

@@ -126,14 +126,6 @@ def test_near_identical_drafts(sv, dtype, noise):
     root and of each depth-1 node forced towards rejection (u near 1): the residual left by a rejected
     sibling is small (about the rows' total variation), so its support and normalisation depend on the
     exact ratio of the two rows' normalisers, not on an estimate of it."""
-    d = inputgen.tree_inputs(48, 30000, seed=81 + int(noise * 100), n_nodes=21, fanout=(4, 4, 1), dtype=dtype,
-                             noise_sd=noise)
-    d["u_accept"] = d["u_accept"].copy()
-    for b in range(d["parents"].shape[0]):
-        for v in range(1, d["parents"].shape[1]):
-            p = int(d["parents"][b, v])
-            first = min(c for c in range(1, d["parents"].shape[1]) if d["parents"][b, c] == p)
-            if v == first or (v - first) % 2 == 1:
-                d["u_accept"][b, v] = 0.999
+    d = inputgen.near_identical_trees(48, 30000, 81 + int(noise * 100), dtype=dtype, noise_sd=noise)
     _, _, na = _check(sv, d, f"near-identical {dtype} sd={noise}")
     assert (na >= 0).all()
