@@ -1005,11 +1005,20 @@ __device__ __forceinline__ void wave_tiles(const char* trow, const char* drow, i
     load_tile_wave<DT>(trow, k * tok, V, lane, t);
     if (RES) load_tile_wave<DT>(drow, k * tok, V, lane, d);
   };
+  // the next tile's loads are issued into the registers of the current one as
+  // soon as its pass has finished with them (before its sums and record)
+  int k = live(k0);
+  if (k >= ntile) return;
+  uint4 t[4], d[4];
+  load(k, t, d);
 #pragma unroll 1
-  for (int k = live(k0); k < ntile; k = live(k + step)) {
-    uint4 t[4], d[4];
-    load(k, t, d);
-    tile_pass<DT, RES, NW>(t, d, J, R + k, TS, tab, wv, lane, [] {});
+  for (;;) {
+    const int kn = live(k + step);
+    tile_pass<DT, RES, NW>(t, d, J, R + k, TS, tab, wv, lane, [&] {
+      if (kn < ntile) load(kn, t, d);
+    });
+    if (kn >= ntile) break;
+    k = kn;
   }
 }
 
