@@ -10,6 +10,7 @@
 #include <stdlib.h>
 
 #include <atomic>
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -18,8 +19,9 @@ using namespace sv;
 namespace sv {
 hipError_t launch_tree_lossless(int dt, const void* tgt, const void* dft, int V, const Layout& L, int max_depth,
                                 const int32_t* tokens, const int32_t* parents, const float* ua, const float* us,
-                                const float* temperature, const Partial* part, int nchunk, double* tiles, int* ctr,
-                                int32_t* out, int32_t* out_nodes, int32_t* num_acc, hipStream_t st);
+                                const float* temperature, const Partial* part, int nchunk, double* sums,
+                                double* rbuf, int* ctr, int32_t* out, int32_t* out_nodes, int32_t* num_acc,
+                                hipStream_t st);
 int lossless_segments(int V, int dt);
 }  // namespace sv
 namespace svp {
@@ -195,17 +197,21 @@ size_t spec_verify_tree_workspace_bytes(int32_t B, int32_t N, int32_t V, int32_t
 }
 
 // Lossless tree workspace: row-chunk partials | per-team segment sums (two
-// buffers) | per-team counters.
+// buffers) | per-team counters | per-team residuals (two buffers of one row in
+// fp64, for at most kLLMaxTeams teams).
 struct CarveLL {
-  size_t part, sums, ctr, total;
+  size_t part, sums, ctr, rbuf, total;
 };
 static CarveLL carve_ll(int B, int N, int V, int dt) {
   CarveLL c;
   c.part = 0;
   const long long rows = (long long)B * (2 * N - 1);
+  const size_t nseg = (size_t)lossless_segments(V, dt);
+  const size_t seg_tok = 64 * (dt == SV_BF16 ? 8 : 4);
   c.sums = align256((size_t)rows * chunking(rows, V, dt).nch * sizeof(Partial));
-  c.ctr = c.sums + align256((size_t)B * 2 * lossless_segments(V, dt) * sizeof(double));
-  c.total = c.ctr + align256((size_t)B * sizeof(int));
+  c.ctr = c.sums + align256((size_t)B * 2 * nseg * sizeof(double));
+  c.rbuf = c.ctr + align256((size_t)B * sizeof(int));
+  c.total = c.rbuf + align256((size_t)std::min(B, kLLMaxTeams) * 2 * nseg * seg_tok * sizeof(double));
   return c;
 }
 
@@ -364,14 +370,14 @@ int spec_verify_tree_lossless(const void* target_logits, const void* draft_logit
   char* ws = static_cast<char*>(workspace);
   Partial* part = reinterpret_cast<Partial*>(ws + cv.part);
   double* sums = reinterpret_cast<double*>(ws + cv.sums);
+  double* rbuf = reinterpret_cast<double*>(ws + cv.rbuf);
   int* ctr = reinterpret_cast<int*>(ws + cv.ctr);
   Layout L{LAYOUT_TREE, B, N, nullptr, 0, RT, RD};
   if ((rc = launch_stats(dtype, target_logits, draft_logits, V, L, temperature, part, st, ctr))) return rc;
   timing_mark(st, true);
   const hipError_t e = launch_tree_lossless(dtype, target_logits, draft_logits, V, L, max_depth, node_tokens, parents,
                                             u_accept, u_sample, temperature, part, chunking(RT + RD, V, dtype).nch,
-                                            sums, ctr,
-                                            out_tokens, out_nodes, num_accepted, st);
+                                            sums, rbuf, ctr, out_tokens, out_nodes, num_accepted, st);
   timing_mark(st, false);
   return e == hipSuccess ? SV_OK : SV_EHIP;
 }

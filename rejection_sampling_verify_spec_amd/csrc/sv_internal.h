@@ -250,6 +250,10 @@ __host__ __device__ inline long long xcd_grid(long long jobs, int G) {
   return (jobs + kXcds - 1) / kXcds * kXcds * G;
 }
 
+// Lossless tree walk: at most this many teams run at once (the workspace holds
+// two residual buffers of one row per team).
+constexpr int kLLMaxTeams = 256;
+
 // Host-side launchers (defined next to their kernels).
 hipError_t launch_row_stats(int dt, const void* tgt, const void* dft, int V, const Layout& L,
                             const float* temperature, int chunk_vecs, int nchunk, Partial* part, int* zero_counts,

@@ -48,6 +48,7 @@ struct LLArgs {
   int nchunk;
   long long RT;      // rows of the target array (draft partials follow)
   double* sums;      // [nteams][2][nseg] segment sums, double-buffered over passes
+  double* rbuf;      // [nteams][2][nseg * 64 * epv] the current node's residual R, per token (see team_pass)
   int* ctr;          // [nteams] passes completed x G, zero at launch
   int G, nteams, nseg;
   int32_t* out;
@@ -71,6 +72,7 @@ struct LLSpace {
   double tab[64];
   int cnt[kLLWaves];
   int bad, flag, nk, wait_ok;
+  int eff, have_store;  // which R buffer holds the current residual, and whether one does
 };
 
 __device__ __forceinline__ uint64_t f64_bits(double v) { return (uint64_t)__double_as_longlong(v); }
@@ -170,11 +172,15 @@ constexpr int kSegBatch = 2;  // segments of one wave whose loads are in flight 
 // R at the lane's vector of up to kSegBatch segments (seg[i] < 0: none) of the
 // current node: R[i*epv + e] for token (seg[i]*64 + lane)*epv + e. The vectors
 // of one row are loaded together, and the next rejected sibling's row is in
-// flight while the current one is applied.
+// flight while the current one is applied. With `rin` (the residual this wave
+// stored for the same segments in an earlier pass), R starts from it and only
+// the steps step_from .. nrej-1 are applied: the same operations in the same
+// order as from the rows, so the same values.
 template <int DT>
 __device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P, const char* trow, long long d0,
                                               int v, int nrej, const int (&seg)[kSegBatch], int lane, double c64,
-                                              double (&R)[kSegBatch * Elem<DT>::kPerVec]) {
+                                              double (&R)[kSegBatch * Elem<DT>::kPerVec], const double* rin = nullptr,
+                                              int step_from = 0) {
   constexpr int epv = Elem<DT>::kPerVec;
   constexpr int es = sizeof(typename Elem<DT>::T);
   auto drow = [&](int k) {
@@ -183,16 +189,30 @@ __device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P,
   // tokens past V (and absent segments) read as -inf: zero mass
   auto tokj = [&](int i) { return seg[i] < 0 ? A.V : (seg[i] * 64 + lane) * epv; };
   uint4 w[kSegBatch], wn[kSegBatch];
+  if (!rin) {
 #pragma unroll
-  for (int i = 0; i < kSegBatch; ++i) w[i] = load_vec<DT>(trow, tokj(i), A.V);
-  int k = next_live(P, 0, nrej);
+    for (int i = 0; i < kSegBatch; ++i) w[i] = load_vec<DT>(trow, tokj(i), A.V);
+  }
+  int k = next_live(P, rin ? step_from : 0, nrej);
   if (k < nrej) {
     const char* dr = drow(k);
 #pragma unroll
     for (int i = 0; i < kSegBatch; ++i) wn[i] = load_vec<DT>(dr, tokj(i), A.V);
   }
   const Exp2Regs K = pinned_exp2();
-  {
+  if (rin) {
+#pragma unroll
+    for (int i = 0; i < kSegBatch; ++i) {
+      const double2* src =
+          reinterpret_cast<const double2*>(rin + (size_t)(seg[i] < 0 ? 0 : seg[i]) * Seg<DT>::tok + lane * epv);
+#pragma unroll
+      for (int q = 0; q < epv / 2; ++q) {
+        const double2 v2 = src[q];
+        R[i * epv + 2 * q] = seg[i] < 0 ? 0.0 : v2.x;
+        R[i * epv + 2 * q + 1] = seg[i] < 0 ? 0.0 : v2.y;
+      }
+    }
+  } else {
     const float mt = P.mt[v];
     const double izt = 1.0 / P.zt[v];
 #pragma unroll
@@ -229,12 +249,18 @@ __device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P,
 // One pass: the team's waves take the segments in turn (wave g of the team:
 // segments g, g + nw, ...), kSegBatch at a time, and store each segment's sum
 // of R; then the team meets. Returns false when the wait ran out of polls.
+// A wave takes the same segments in every pass, so it can keep R for them:
+// with `rin`, R is its stored residual plus the steps step_from .. nrej-1
+// (one new rejected sibling's row instead of all of them), else it is formed
+// from the rows; with `rout`, the new R is stored there.
 template <int DT>
 __device__ bool team_pass(const LLArgs& A, LLSpace& P, long long t0, long long d0, int v, int nrej, double* buf,
-                          int* ctr, int target, int rank, double c64) {
+                          int* ctr, int target, int rank, double c64, const double* rin, int step_from,
+                          double* rout) {
   constexpr int epv = Elem<DT>::kPerVec;
   constexpr int es = sizeof(typename Elem<DT>::T);
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // (uniform: segment indices in scalar registers)
   const int nw = A.G * kLLWaves;
   const char* trow = reinterpret_cast<const char*>(A.tgt) + (size_t)(t0 + v) * (size_t)A.V * es;
   for (int s0 = rank * kLLWaves + wv; s0 < A.nseg; s0 += nw * kSegBatch) {
@@ -242,7 +268,16 @@ __device__ bool team_pass(const LLArgs& A, LLSpace& P, long long t0, long long d
 #pragma unroll
     for (int i = 0; i < kSegBatch; ++i) seg[i] = s0 + i * nw < A.nseg ? s0 + i * nw : -1;
     double R[kSegBatch * epv];
-    residual_segs<DT>(A, P, trow, d0, v, nrej, seg, lane, c64, R);
+    residual_segs<DT>(A, P, trow, d0, v, nrej, seg, lane, c64, R, rin, step_from);
+    if (rout) {
+#pragma unroll
+      for (int i = 0; i < kSegBatch; ++i) {
+        if (seg[i] < 0) continue;
+        double* dst = rout + (size_t)seg[i] * Seg<DT>::tok + lane * epv;
+#pragma unroll
+        for (int e = 0; e < epv; ++e) dst[e] = R[i * epv + e];
+      }
+    }
 #pragma unroll
     for (int i = 0; i < kSegBatch; ++i) {
       double s = 0.0;
@@ -377,6 +412,8 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
   bool alive = true;
   double* const sums = A.sums + (size_t)team * 2 * A.nseg;
   int* const ctr = A.ctr + team;
+  const size_t slab = (size_t)A.nseg * Seg<DT>::tok;  // one R buffer
+  double* const rbuf = A.rbuf + (size_t)team * 2 * slab;
   for (int b = team; b < A.B; b += A.nteams) {
     const float T = A.temperature[b];
     const bool greedy = T == 0.0f;
@@ -474,7 +511,11 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
     bool failed = false;
     for (;;) {
       list_children(P, N, v);
-      if (tid == 0) P.S[0] = 1.0;
+      if (tid == 0) {
+        P.S[0] = 1.0;
+        P.eff = 0;
+        P.have_store = 0;  // a new node: no stored residual yet
+      }
       nrej = 0;
       have_sums = false;
       int accepted = -1;
@@ -485,11 +526,14 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
           accepted = c;
           break;
         }
-        // rejected: the next residual's total
+        // rejected: the next residual's total (from the stored residual when
+        // one holds the current R, the new one stored in the other buffer)
         ++nrej;
         ++passes;
+        const double* rin = P.have_store ? rbuf + (size_t)P.eff * slab : nullptr;
+        double* rout = rbuf + (size_t)(1 - P.eff) * slab;
         if (!team_pass<DT>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr, passes * A.G, rank,
-                           c64)) {
+                           c64, rin, nrej - 1, rout)) {
           failed = true;
           break;
         }
@@ -506,6 +550,12 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
         }
         __syncthreads();
         have_sums = !P.skip[nrej - 1];
+        // the new residual is the current one unless its sum underflowed (r kept)
+        if (tid == 0 && have_sums) {
+          P.eff = 1 - P.eff;
+          P.have_store = 1;
+        }
+        __syncthreads();
       }
       if (failed) break;
       if (accepted < 0) break;
@@ -519,7 +569,7 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
     if (!failed && !have_sums) {
       ++passes;
       failed = !team_pass<DT>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr, passes * A.G,
-                              rank, c64);
+                              rank, c64, P.have_store ? rbuf + (size_t)P.eff * slab : nullptr, nrej, nullptr);
     }
     if (failed) {
       // a team wait ran out of polls: this team's remaining requests report -1
@@ -549,8 +599,9 @@ int lossless_segments(int V, int dt) {
 
 hipError_t launch_tree_lossless(int dt, const void* tgt, const void* dft, int V, const Layout& L, int max_depth,
                                 const int32_t* tokens, const int32_t* parents, const float* ua, const float* us,
-                                const float* temperature, const Partial* part, int nchunk, double* sums, int* ctr,
-                                int32_t* out, int32_t* out_nodes, int32_t* num_acc, hipStream_t st) {
+                                const float* temperature, const Partial* part, int nchunk, double* sums,
+                                double* rbuf, int* ctr, int32_t* out, int32_t* out_nodes, int32_t* num_acc,
+                                hipStream_t st) {
   if (L.B == 0) return hipSuccess;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
@@ -568,6 +619,7 @@ hipError_t launch_tree_lossless(int dt, const void* tgt, const void* dft, int V,
   if (G > resident) G = (int)resident;
   long long nteams = resident / G;
   if (nteams > L.B) nteams = L.B;
+  if (nteams > kLLMaxTeams) nteams = kLLMaxTeams;  // (the workspace holds that many teams' residuals)
   LLArgs A;
   A.tgt = tgt;
   A.dft = dft;
@@ -584,6 +636,7 @@ hipError_t launch_tree_lossless(int dt, const void* tgt, const void* dft, int V,
   A.nchunk = nchunk;
   A.RT = L.RT;
   A.sums = sums;
+  A.rbuf = rbuf;
   A.ctr = ctr;
   A.G = G;
   A.nteams = (int)nteams;
