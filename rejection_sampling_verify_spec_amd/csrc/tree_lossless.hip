@@ -117,28 +117,40 @@ __device__ __forceinline__ double sum_segments(const double* buf, int nseg, int 
   return wave_sum(s);
 }
 
+// The logit that lane l of wave 0 needs for the test of child c after nrej
+// rejected siblings (l < nrej + 2 <= 64): the token's logit in the target row
+// (l = 0), in rejected sibling l's draft row, or in c's draft row (l = nrej + 1).
+template <int DT>
+__device__ __forceinline__ float child_logit(const LLArgs& A, const LLSpace& P, long long t0, long long d0, int v,
+                                             int nrej, int c, int l) {
+  const int x = P.tok[c];
+  if (l == 0) return Elem<DT>::at(A.tgt, (t0 + v) * (long long)A.V + x);
+  if (l >= nrej + 2) return 0.0f;
+  const int w = l <= nrej ? P.rej[l - 1] : c;
+  return Elem<DT>::at(A.dft, (d0 + w - 1) * (long long)A.V + x);
+}
+
 // The acceptance test of child c of node v after nrej rejected siblings: wave 0
 // loads the token's logit in the target row, in each rejected sibling's draft
 // row and in c's draft row at once (64 at a time) and forms their
 // probabilities; the residual steps are then applied in order across the
-// lanes (result in P.flag).
+// lanes (result in P.flag). With `pre`, lane l's logit of the first 64 was
+// loaded earlier (while the pass before this test ran): `lg`.
 template <int DT>
 __device__ __forceinline__ void child_test(const LLArgs& A, LLSpace& P, long long t0, long long d0, int v, int nrej,
-                                           int c, double c64) {
+                                           int c, double c64, bool pre = false, float lg = 0.0f) {
   const int tid = threadIdx.x, lane = tid & 63;
-  const int x = P.tok[c];
   if (tid < 64) {
     double R = 0.0, q = 0.0;
     for (int l0 = 0; l0 < nrej + 2; l0 += 64) {
       const int l = l0 + lane;
+      const float lv = pre && l0 == 0 ? lg : child_logit<DT>(A, P, t0, d0, v, nrej, c, l);
       double m = 0.0;
       if (l == 0) {
-        const float lt = Elem<DT>::at(A.tgt, (t0 + v) * (long long)A.V + x);
-        m = emass_t(lt, P.mt[v], c64, P.tab) * (1.0 / P.zt[v]);
+        m = emass_t(lv, P.mt[v], c64, P.tab) * (1.0 / P.zt[v]);
       } else if (l < nrej + 2) {
         const int w = l <= nrej ? P.rej[l - 1] : c;
-        const float ld = Elem<DT>::at(A.dft, (d0 + w - 1) * (long long)A.V + x);
-        m = emass_t(ld, P.md[w], c64, P.tab) * (1.0 / P.zd[w]);
+        m = emass_t(lv, P.md[w], c64, P.tab) * (1.0 / P.zd[w]);
       }
       const int n = min(64, nrej + 2 - l0);
       for (int k = 0; k < n; ++k) {
@@ -519,9 +531,11 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
       nrej = 0;
       have_sums = false;
       int accepted = -1;
+      bool pre = false;  // lg holds wave 0's logits for the next child's test
+      float lg = 0.0f;
       for (int i = 0; i < P.nk; ++i) {
         const int c = P.kids[i];
-        child_test<DT>(A, P, t0, d0, v, nrej, c, c64);
+        child_test<DT>(A, P, t0, d0, v, nrej, c, c64, pre, lg);
         if (P.flag) {
           accepted = c;
           break;
@@ -530,6 +544,9 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
         // one holds the current R, the new one stored in the other buffer)
         ++nrej;
         ++passes;
+        // the next child's logits, loaded while the pass runs
+        pre = i + 1 < P.nk && nrej + 2 <= 64;
+        if (pre && tid < 64) lg = child_logit<DT>(A, P, t0, d0, v, nrej, P.kids[i + 1], lane);
         const double* rin = P.have_store ? rbuf + (size_t)P.eff * slab : nullptr;
         double* rout = rbuf + (size_t)(1 - P.eff) * slab;
         if (!team_pass<DT>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr, passes * A.G, rank,
