@@ -417,7 +417,10 @@ template <int DT>
 __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_tree_lossless(LLArgs A) {
   __shared__ LLSpace P;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  const int team = blockIdx.x / A.G, rank = blockIdx.x - team * A.G;
+  // a team's workgroups on one XCD when the teams fill whole XCD rounds
+  // (workgroup i of the grid runs on XCD i mod 8)
+  const JobPart jp = A.nteams % kXcds == 0 ? xcd_job_part(blockIdx.x, A.G) : JobPart{(int)blockIdx.x / A.G, (int)blockIdx.x % A.G};
+  const int team = jp.job, rank = jp.part;
   const int N = A.N, width = A.max_depth + 1;
   if (tid < 64) P.tab[tid] = exp2_f64((double)tid * 0.015625);
   int passes = 0;  // passes of this team so far (the same in all its workgroups)
