@@ -2,6 +2,7 @@
 and invariants (no GPU)."""
 import numpy as np
 import scipy.special
+import scipy.stats
 
 import inputgen
 import oracle
@@ -182,3 +183,96 @@ def test_ragged_cu_validation():
     ok = oracle.verify_chain(d["target"], d["draft"], d["draft_tokens"], d["u_accept"], d["u_sample"],
                              d["temperature"], gamma=d["gamma_max"], cu_gamma=d["cu_gamma"])
     assert (ok["num_accepted"] >= 0).all()
+
+
+# Lowest-child tree rule (one reading of [Primer 考点3], tree verified in one pass): its
+# output distribution on a five-node tree, derived by enumerating which nodes pass their
+# tests, against the oracle's histogram over many seeded uniforms.
+_PAR = (-1, 0, 0, 0, 2)   # root 0; children 1, 2, 3; node 4 under node 2
+
+
+def _lowest_child_distribution(pt, pd, tok, *, tie="lowest", depth_first=True, residual_child="lowest",
+                               test_row="parent"):
+    """P(end node e, final token y) for the tree _PAR, by enumerating the 2^4 pass/fail outcomes.
+
+    pt [5, V], pd [4, V] (row v-1 belongs to node v). The keyword arguments select a
+    plausible mistake instead of the rule; the defaults are the rule itself."""
+    N, V = pt.shape
+    par = _PAR
+    a = np.zeros(N)
+    for v in range(1, N):
+        row = pt[par[v]] if test_row == "parent" else pt[v]
+        a[v] = min(1.0, row[tok[v]] / pd[v - 1, tok[v]])
+    depth = [0, 1, 1, 1, 2]
+    dist = np.zeros((N, V))
+    for mask in range(1 << (N - 1)):
+        acc = [True] + [bool(mask >> (v - 1) & 1) for v in range(1, N)]
+        prob = np.prod([a[v] if acc[v] else 1.0 - a[v] for v in range(1, N)])
+        kept = [v for v in range(N) if all(acc[w] for w in _path(v))]
+        key = (lambda v: (-depth[v], v if tie == "lowest" else -v)) if depth_first else \
+              (lambda v: (v == 0, v if tie == "lowest" else -v))
+        e = min(kept, key=key)
+        kids = [c for c in range(1, N) if par[c] == e]
+        if kids:
+            c = min(kids) if residual_child == "lowest" else max(kids)
+            q = np.maximum(pt[e] - pd[c - 1], 0.0)
+        else:
+            q = pt[e].copy()
+        dist[e] += prob * q / q.sum()
+    return dist
+
+
+def _path(v):
+    out = []
+    while v > 0:
+        out.append(v)
+        v = _PAR[v]
+    return out
+
+
+def test_lowest_child_rule_distribution():
+    B, V = 200_000, 5
+    rng = np.random.default_rng(20261205)
+    tl = rng.normal(0.0, 1.0, (5, V)).astype(np.float32)
+    dl = rng.normal(0.0, 1.0, (4, V)).astype(np.float32)
+    pt = scipy.special.softmax(tl.astype(np.float64), axis=-1)
+    pd = scipy.special.softmax(dl.astype(np.float64), axis=-1)
+    # each node drafts the token whose acceptance probability is nearest 1/2
+    tok = np.zeros(5, np.int32)
+    for v in range(1, 5):
+        tok[v] = np.argmin(np.abs(np.minimum(1.0, pt[_PAR[v]] / pd[v - 1]) - 0.5))
+    expect = _lowest_child_distribution(pt, pd, tok)
+    a = [min(1.0, pt[_PAR[v], tok[v]] / pd[v - 1, tok[v]]) for v in range(1, 5)]
+    assert all(0.1 < x < 0.95 for x in a), a   # every branch of the rule is exercised
+    r = oracle.verify_tree(np.broadcast_to(tl, (B, 5, V)).copy(), np.broadcast_to(dl, (B, 4, V)).copy(),
+                           np.broadcast_to(tok, (B, 5)).copy(), np.broadcast_to(np.int32(_PAR), (B, 5)).copy(),
+                           rng.random((B, 5), dtype=np.float32), rng.random((B, 5), dtype=np.float32),
+                           np.ones(B, np.float32), max_depth=2)
+    n = r["num_accepted"]
+    e = np.where(n > 0, r["out_nodes"][np.arange(B), np.maximum(n - 1, 0)], 0)
+    y = r["out_tokens"][np.arange(B), n]
+    obs = np.zeros((5, V))
+    np.add.at(obs, (e, y), 1)
+    # the emitted drafted tokens are the nodes on the root path of e
+    for v in range(1, 5):
+        sel = e == v
+        path = _path(v)[::-1]
+        assert (r["out_tokens"][sel][:, :len(path)] == tok[path]).all()
+
+    def chi2(dist):
+        """Pearson statistic and degrees of freedom; infinite when a token the distribution
+        gives no mass was drawn."""
+        exp = B * dist.reshape(-1)
+        m = exp > 0
+        if obs.reshape(-1)[~m].sum() > 0:
+            return np.inf, int(m.sum()) - 1
+        return ((obs.reshape(-1)[m] - exp[m]) ** 2 / exp[m]).sum(), int(m.sum()) - 1
+
+    stat, df = chi2(expect)
+    assert scipy.stats.chi2.sf(stat, df) > 1e-3, (stat, df)
+    # the same counts reject each plausible mistake in the rule
+    crit = scipy.stats.chi2.isf(1e-6, df)
+    for kw in (dict(residual_child="highest"), dict(tie="highest"), dict(depth_first=False),
+               dict(test_row="own")):
+        bad, _ = chi2(_lowest_child_distribution(pt, pd, tok, **kw))
+        assert bad > crit, (kw, bad, crit)
