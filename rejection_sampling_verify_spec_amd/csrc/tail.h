@@ -707,12 +707,14 @@ __device__ __forceinline__ void exact_token(bool has, float xt, float xd, const 
     if (RES) {
       ed = emass_t(xd, J.md, J.c64, tab, K);
       A.zd += ed;
-      if (et > hi * ed) {
-        A.dp += et - J.rho * ed;
-        A.bp += ed;
-      } else {
-        und = et > 0.0 && et >= lo * ed;
-      }
+      // a token on the positive side adds et - rho ed and ed, as fma(1, ., .);
+      // the others add nothing, as fma(0, ., .) (masses are finite): the same
+      // sums as adding under a branch, without one
+      const bool pos = et > hi * ed;
+      const double pf = pos ? 1.0 : 0.0;
+      A.dp = __builtin_fma(pf, __builtin_fma(-J.rho, ed, et), A.dp);
+      A.bp = __builtin_fma(pf, ed, A.bp);
+      und = !pos && et > 0.0 && et >= lo * ed;
     }
   }
   if (!RES) return;
