@@ -274,15 +274,16 @@ __device__ __forceinline__ double exp2_tab(double a, const double* tab, const Ex
   // of t hold k as a two's-complement int
   double t;
   __asm__("v_fma_f64 %0, %1, %2, %3" : "=v"(t) : "v"(a), "s"(64.0), "v"(K.shift));
+  const int ki = (int)(uint32_t)(uint64_t)__double_as_longlong(t);
+  const double tv = tab[ki & 63];  // (read before the polynomial, which then covers its latency)
   const double k = t - 0x1.8p52;
   const double r = __builtin_fma(k, -0.015625, a);
-  const int ki = (int)(uint32_t)(uint64_t)__double_as_longlong(t);
   double p = fma_first_f64(r, 0x1.5d87fe78a6731p-10, K.c4);  // ln2^5 / 5!, ln2^4 / 4!
   p = fma3_f64(p, r, 0x1.c6b08d704a0c0p-5);  // ln2^3 / 3!
   p = fma3_f64(p, r, 0x1.ebfbdff82c58fp-3);  // ln2^2 / 2!
   p = fma3_f64(p, r, 0x1.62e42fefa39efp-1);  // ln2
   p = __builtin_fma(p, r, 1.0);
-  return __builtin_ldexp(tab[ki & 63] * p, ki >> 6);
+  return __builtin_ldexp(tv * p, ki >> 6);
 }
 __device__ __forceinline__ double exp2_tab(double a, const double* tab) {
   return exp2_tab(a, tab, Exp2Regs{0x1.8p52, 0x1.3b2ab6fba4e77p-7});
@@ -688,36 +689,36 @@ __device__ __forceinline__ void load_tile_wave(const void* rowp, int j0, int V, 
 // ---------------------------------------------------------------------------
 // Tile pass.
 
-// Double-precision treatment of one flagged token (has == false: this lane has
-// none left this step, but still takes part in the wave ballot).
+// A lane's double-precision sums over its flagged tokens.
 struct ExactAcc {
   double zt, zd, dp, bp;
   int n;  // undecided tokens seen (wave-uniform)
 };
 
-template <bool RES, int NW>
-__device__ __forceinline__ void exact_token(bool has, float xt, float xd, const SampleJob& J, double hi, double lo,
-                                            unsigned long long below, ExactAcc& A, TileLists<NW>& L, int wv,
-                                            const double* tab, const Exp2Regs& K) {
-  double et = 0.0, ed = 0.0;
-  bool und = false;
-  if (has) {
-    et = emass_t(xt, J.mt, J.c64, tab, K);
-    A.zt += et;
-    if (RES) {
-      ed = emass_t(xd, J.md, J.c64, tab, K);
-      A.zd += ed;
-      // a token on the positive side adds et - rho ed and ed, as fma(1, ., .);
-      // the others add nothing, as fma(0, ., .) (masses are finite): the same
-      // sums as adding under a branch, without one
-      const bool pos = et > hi * ed;
-      const double pf = pos ? 1.0 : 0.0;
-      A.dp = __builtin_fma(pf, __builtin_fma(-J.rho, ed, et), A.dp);
-      A.bp = __builtin_fma(pf, ed, A.bp);
-      und = !pos && et > 0.0 && et >= lo * ed;
-    }
-  }
-  if (!RES) return;
+// The sums of one token in double precision; returns whether it is undecided
+// (inside the band around rho~), with its masses in et and ed.
+template <bool RES>
+__device__ __forceinline__ bool exact_sums(float xt, float xd, const SampleJob& J, double hi, double lo, ExactAcc& A,
+                                           const double* tab, const Exp2Regs& K, double& et, double& ed) {
+  et = emass_t(xt, J.mt, J.c64, tab, K);
+  A.zt += et;
+  if (!RES) return false;
+  ed = emass_t(xd, J.md, J.c64, tab, K);
+  A.zd += ed;
+  // a token on the positive side adds et - rho ed and ed, as fma(1, ., .);
+  // the others add nothing, as fma(0, ., .) (masses are finite): the same
+  // sums as adding under a branch, without one
+  const bool pos = et > hi * ed;
+  const double pf = pos ? 1.0 : 0.0;
+  A.dp = __builtin_fma(pf, __builtin_fma(-J.rho, ed, et), A.dp);
+  A.bp = __builtin_fma(pf, ed, A.bp);
+  return !pos && et > 0.0 && et >= lo * ed;
+}
+
+// Appends this step's undecided tokens to the wave's list, in lane order.
+template <int NW>
+__device__ __forceinline__ void append_undecided(bool und, float xt, float xd, double et, double ed,
+                                                 unsigned long long below, ExactAcc& A, TileLists<NW>& L, int wv) {
   const unsigned long long m = __ballot(und);
   if (m) {
     const int slot = A.n + __builtin_popcountll(m & below);
@@ -728,6 +729,18 @@ __device__ __forceinline__ void exact_token(bool has, float xt, float xd, const 
     }
     A.n += __builtin_popcountll(m);
   }
+}
+
+// Double-precision treatment of one flagged token (has == false: this lane has
+// none left this step, but still takes part in the wave ballot).
+template <bool RES, int NW>
+__device__ __forceinline__ void exact_token(bool has, float xt, float xd, const SampleJob& J, double hi, double lo,
+                                            unsigned long long below, ExactAcc& A, TileLists<NW>& L, int wv,
+                                            const double* tab, const Exp2Regs& K) {
+  double et = 0.0, ed = 0.0;
+  bool und = false;
+  if (has) und = exact_sums<RES>(xt, xd, J, hi, lo, A, tab, K, et, ed);
+  if (RES) append_undecided<NW>(und, xt, xd, et, ed, below, A, L, wv);
 }
 
 // Token e of a staged 16-byte vector, read from LDS.
@@ -914,14 +927,38 @@ __device__ __forceinline__ void tile_pass(uint4 (&wt)[4], uint4 (&wd)[4], const 
     // when every token is flagged
     const double hi = J.rho * (1.0 + kRhoBand), lo = J.rho * (1.0 - kRhoBand);
     const unsigned long long below = (1ull << lane) - 1ull;
+    // (no ballot between tokens, so that the tokens of a vector can overlap;
+    // the undecided ones are appended afterwards, in the same order)
+    uint32_t und = 0u;
 #pragma unroll 1
     for (int u = 0; u < nv; ++u) {
       float xt[epv], xd[epv];
       unpack<DT>(G.t[wv][u][lane], xt);
       if (RES) unpack<DT>(G.d[wv][u][lane], xd);
 #pragma unroll
-      for (int e = 0; e < epv; ++e)
-        exact_token<RES, NW>(true, xt[e], RES ? xd[e] : 0.f, J, hi, lo, below, A, L, wv, tab, K);
+      for (int e = 0; e < epv; ++e) {
+        double et, ed;
+        und |= (uint32_t)exact_sums<RES>(xt[e], RES ? xd[e] : 0.f, J, hi, lo, A, tab, K, et, ed) << (u * epv + e);
+      }
+    }
+    if (RES) {
+      // token i of every lane at step i, as the flagged loop orders them; the
+      // masses again from the staged logits (the same arithmetic, the same values)
+#pragma unroll 1
+      while (__any(und != 0u)) {
+        const int i = wave_minmax<false>(und != 0u ? __builtin_ctz(und) : 32);
+        const bool mine = (und >> i) & 1u;
+        und &= ~(1u << i);
+        float xt = 0.f, xd = 0.f;
+        double et = 0.0, ed = 0.0;
+        if (mine) {
+          xt = staged_at<DT>(G.t[wv][i / epv][lane], i % epv);
+          xd = staged_at<DT>(G.d[wv][i / epv][lane], i % epv);
+          et = emass_t(xt, J.mt, J.c64, tab, K);
+          ed = emass_t(xd, J.md, J.c64, tab, K);
+        }
+        append_undecided<NW>(mine, xt, xd, et, ed, below, A, L, wv);
+      }
     }
     __builtin_amdgcn_wave_barrier();
   } else if (any_flagged) {
