@@ -10,7 +10,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["api.hip", "row_stats.hip", "accept.hip", "finish.hip", "verify.hip", "sample.hip", "cache.hip", "tree_lossless.hip", "probe.hip"]
+SOURCES = ["api.hip", "row_stats.hip", "accept.hip", "finish.hip", "verify.hip", "cache.hip", "tree_lossless.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

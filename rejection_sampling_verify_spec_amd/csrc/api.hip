@@ -416,17 +416,14 @@ int spec_sample_rows(const void* logits, int32_t dtype, int32_t rows, int32_t V,
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   Partial* part = reinterpret_cast<Partial*>(ws + cv.part);
-  SampleJob* jobs = reinterpret_cast<SampleJob*>(ws + cv.jobs);
   TileRec* recs = reinterpret_cast<TileRec*>(ws + cv.recs);
   int* done = reinterpret_cast<int*>(ws + cv.done);
   Layout L{LAYOUT_ROWS, rows, 0, nullptr, 0, rows, 0};
   if ((rc = launch_stats(dtype, logits, nullptr, V, L, temperature, part, st, done))) return rc;
   const Chunking ch = chunking(rows, V, dtype);
-  if (launch_sample_jobs(dtype, logits, V, part, ch.nch, ch.cv, rows, temperature, u, jobs,
-                         out_tokens, st) != hipSuccess)
-    return SV_EHIP;
-  if (launch_finish_jobs(dtype, logits, logits, V, rows, jobs, recs, part, ch.nch, rows, done,
-                         out_tokens, 1, force_exact_residual(), st) != hipSuccess)
+  // each row's job is built by its draw workgroups (no job table)
+  if (launch_finish_jobs(dtype, logits, logits, V, rows, nullptr, recs, part, ch.nch, rows, done, out_tokens, 1,
+                         force_exact_residual(), st, ch.cv, temperature, u) != hipSuccess)
     return SV_EHIP;
   return SV_OK;
 }

@@ -267,12 +267,13 @@ hipError_t launch_verify_chain(int dt, const void* tgt, const void* dft, int V, 
                                const Partial* part, int nchunk, int chunk_vecs, TileRec* recs, int* done,
                                int32_t* out, int out_width, int32_t* num_acc, float* diag, int force_exact,
                                hipStream_t st);
+// The draw of each job (jobs != nullptr: written by an earlier kernel), or of
+// each of B logit rows of draft-token sampling (jobs == nullptr: the kernel
+// builds a row's job from its partials, chunk_vecs, temperature[b] and u[b]).
 hipError_t launch_finish_jobs(int dt, const void* tgt, const void* dft, int V, int B, SampleJob* jobs,
                               TileRec* recs, const Partial* part, int nchunk, long long RT, int* done, int32_t* out,
-                              int out_width, int force_exact, hipStream_t st);
-hipError_t launch_sample_jobs(int dt, const void* logits, int V, const Partial* part, int nchunk, int chunk_vecs,
-                              int rows, const float* temperature, const float* u, SampleJob* jobs, int32_t* out,
-                              hipStream_t st);
+                              int out_width, int force_exact, hipStream_t st, int chunk_vecs = 0,
+                              const float* temperature = nullptr, const float* u = nullptr);
 hipError_t launch_stats_finalize(const Partial* part, int nchunk, int rows, const float* temperature,
                                  float* out_max, float* out_logz, int32_t* out_argmax, hipStream_t st);
 
