@@ -1,7 +1,7 @@
 // probe.hip -- a plain read of a buffer with the load pattern of the streaming
-// statistics kernel (256 threads, 2048 16-byte vectors per workgroup, four
-// nontemporal loads in flight per thread), folding the bits into one word per
-// wave so that no load can be dropped. It measures the read rate this part
+// statistics kernel (256 threads, 2048 16-byte vectors per workgroup, all
+// eight of a thread's nontemporal loads in flight at once), folding the bits
+// into one word per wave so that no load can be dropped. It measures the read rate this part
 // reaches in practice, next to the 8 TB/s peak the streaming kernel is priced
 // against.
 #include <hip/hip_runtime.h>
@@ -11,7 +11,7 @@ namespace svp {
 
 constexpr int kThreads = 256;
 constexpr int kVecPerBlock = 2048;
-constexpr int kU = 4;
+constexpr int kU = 8;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(kThreads) void k_read_probe(const u32x4* __restrict__ src, long long nvec,

@@ -3,6 +3,8 @@
 // finalisation of the statistics entry point.
 #include "stream.h"
 
+#include <stdlib.h>
+
 namespace sv {
 
 __device__ __forceinline__ long long request_of_row(const Layout& L, long long r, bool draft) {
@@ -27,10 +29,11 @@ __device__ __forceinline__ long long request_of_row(const Layout& L, long long r
 }
 
 // One workgroup per (row, chunk); rows are the target rows, then the draft rows.
+// NB: groups of 16-byte loads a thread has in flight at once (1 or 2).
 // The first B workgroups also zero `zero_counts` (when given, B + 1 ints), the
 // per-request counters of the chain tail kernel, and workgroup 0 stores the
 // ragged layout's validity in zero_counts[B].
-template <int DT>
+template <int DT, int NB>
 __global__ __launch_bounds__(kTPB) void k_row_stats(const void* __restrict__ tgt, const void* __restrict__ dft,
                                                     int V, Layout L, const float* __restrict__ temperature,
                                                     int chunk_vecs, int nchunk, Partial* __restrict__ part,
@@ -50,7 +53,7 @@ __global__ __launch_bounds__(kTPB) void k_row_stats(const void* __restrict__ tgt
     if (temperature_ok(T) && !(draft && T == 0.0f)) {
       const void* rowp =
           reinterpret_cast<const char*>(draft ? dft : tgt) + (size_t)r * (size_t)V * sizeof(typename E::T);
-      row_chunk_stats<DT>(rowp, V, chunk, chunk_vecs, T, part + item);
+      row_chunk_stats<DT, NB>(rowp, V, chunk, chunk_vecs, T, part + item);
     }
   }
   // The stores for the kernel that follows come last: a store before the
@@ -79,12 +82,35 @@ hipError_t launch_row_stats(int dt, const void* tgt, const void* dft, int V, con
   if (zero_counts && grid < L.B) grid = L.B;  // every counter gets a workgroup
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (dt == 1)
-    hipLaunchKernelGGL(k_row_stats<1>, dim3((unsigned)grid), dim3(kTPB), 0, st, tgt, dft, V, L, temperature,
-                       chunk_vecs, nchunk, part, zero_counts);
-  else
-    hipLaunchKernelGGL(k_row_stats<0>, dim3((unsigned)grid), dim3(kTPB), 0, st, tgt, dft, V, L, temperature,
-                       chunk_vecs, nchunk, part, zero_counts);
+  // Groups of loads in flight per thread: two (a whole 2048-vector chunk at
+  // once; 78 VGPRs, six workgroups per CU for bf16) for the dense, tree and
+  // row layouts, one (57 VGPRs, eight per CU) for chunks of one group and for
+  // the ragged layout, where two
+  // measured slower, likely because its workgroups start with a dependent
+  // binary search of cu_gamma, which more resident workgroups cover. Measured
+  // on one box with two instead of one: large -1.4%, trees -1.0%, sampled
+  // rows -0.7%, ragged +1.3%. SPECVERIFY_STREAM_GROUPS (1 or 2) overrides.
+  static const int nb_env = [] {
+    const char* e = getenv("SPECVERIFY_STREAM_GROUPS");
+    const int v = e ? atoi(e) : 0;
+    return v == 1 || v == 2 ? v : 0;
+  }();
+  const int nb = nb_env ? nb_env : (L.mode == LAYOUT_RAGGED || chunk_vecs < 2 * kTPB * kU ? 1 : 2);
+  if (dt == 1) {
+    if (nb == 2)
+      hipLaunchKernelGGL((k_row_stats<1, 2>), dim3((unsigned)grid), dim3(kTPB), 0, st, tgt, dft, V, L, temperature,
+                         chunk_vecs, nchunk, part, zero_counts);
+    else
+      hipLaunchKernelGGL((k_row_stats<1, 1>), dim3((unsigned)grid), dim3(kTPB), 0, st, tgt, dft, V, L, temperature,
+                         chunk_vecs, nchunk, part, zero_counts);
+  } else {
+    if (nb == 2)
+      hipLaunchKernelGGL((k_row_stats<0, 2>), dim3((unsigned)grid), dim3(kTPB), 0, st, tgt, dft, V, L, temperature,
+                         chunk_vecs, nchunk, part, zero_counts);
+    else
+      hipLaunchKernelGGL((k_row_stats<0, 1>), dim3((unsigned)grid), dim3(kTPB), 0, st, tgt, dft, V, L, temperature,
+                         chunk_vecs, nchunk, part, zero_counts);
+  }
   return hipGetLastError();
 }
 

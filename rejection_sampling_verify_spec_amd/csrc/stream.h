@@ -86,11 +86,19 @@ __device__ __forceinline__ void load_group_tail(const uint4* vp, int vb, int v1,
 }
 
 // Visit the 16-byte vectors [v0, v1) of a chunk in groups; f(w, vb) gets each
-// group. (Loading one group at a time keeps the kernel at 8 waves per SIMD,
-// which hides more latency than deeper per-thread batches at lower occupancy.)
-template <int DT, typename F>
+// group. NB full groups are loaded at once (then the rest one at a time): more
+// bytes in flight per thread, at the price of the registers that hold them.
+template <int DT, int NB = 1, typename F>
 __device__ __forceinline__ void for_each_group(const uint4* vp, int v0, int v1, int tid, F f) {
   int vb = v0;
+  if constexpr (NB > 1) {  // NB groups' loads in flight at once
+    for (; vb + NB * kU * kTPB <= v1; vb += NB * kU * kTPB) {
+      uint4 w[NB * kU];
+      load_groups_full<NB>(vp, vb, tid, w);
+#pragma unroll
+      for (int g = 0; g < NB; ++g) f(w + g * kU, vb + g * kU * kTPB);
+    }
+  }
   for (; vb + kU * kTPB <= v1; vb += kU * kTPB) {
     uint4 w[kU];
     load_groups_full<1>(vp, vb, tid, w);
@@ -218,7 +226,7 @@ __device__ __forceinline__ void sampling_finish(const void* rowp, const RowSplit
 
 // Statistics of vectors [v0, v1) of a row (plus the scalar head / tail when
 // asked) at temperature coefficient c; thread 0 publishes the partial.
-template <int DT>
+template <int DT, int NB>
 __device__ void stats_sampling(const void* rowp, const RowSplit& sp, int v0, int v1, bool do_head, bool do_tail,
                                float c, Partial* out) {
   using E = Elem<DT>;
@@ -229,7 +237,7 @@ __device__ void stats_sampling(const void* rowp, const RowSplit& sp, int v0, int
                                                    (size_t)sp.head * sizeof(typename E::T));
   float m = -INFINITY, K = 0.f, s = 0.f;
   bool ovf = false;
-  for_each_group<DT>(vp, v0, v1, tid, [&](const uint4* w, int) {
+  for_each_group<DT, NB>(vp, v0, v1, tid, [&](const uint4* w, int) {
     float x[G];
 #pragma unroll
     for (int u = 0; u < kU; ++u) unpack<DT>(w[u], x + u * EPV);
@@ -317,7 +325,7 @@ __device__ __forceinline__ void greedy_finish(const void* rowp, const RowSplit& 
   wg_sync();  // sm / si are reused by the workgroup's next chunk
 }
 
-template <int DT>
+template <int DT, int NB>
 __device__ void stats_greedy(const void* rowp, const RowSplit& sp, int v0, int v1, bool do_head, bool do_tail,
                              Partial* out) {
   using E = Elem<DT>;
@@ -328,15 +336,15 @@ __device__ void stats_greedy(const void* rowp, const RowSplit& sp, int v0, int v
   int idx = -1;
   us2_t mag2 = {0, 0};
   uint32_t mag = 0;
-  for_each_group<DT>(vp, v0, v1, tid,
-                     [&](const uint4* w, int vb) { greedy_group<DT>(w, vb, sp.head, tid, m, idx, mag2, mag); });
+  for_each_group<DT, NB>(vp, v0, v1, tid,
+                         [&](const uint4* w, int vb) { greedy_group<DT>(w, vb, sp.head, tid, m, idx, mag2, mag); });
   greedy_finish<DT>(rowp, sp, do_head, do_tail, m, idx, mag2, mag, out);
 }
 
 // Statistics of chunk `chunk` of one row (the chunk covers 16-byte vectors
 // [chunk * chunk_vecs, (chunk + 1) * chunk_vecs) of the row's vector part;
 // chunk 0 also takes the scalar head, the last chunk the scalar tail).
-template <int DT>
+template <int DT, int NB = 1>
 __device__ __forceinline__ void row_chunk_stats(const void* rowp, int V, int chunk, int chunk_vecs, float T,
                                                 Partial* out) {
   const RowSplit sp = split_row<DT>(rowp, V);
@@ -344,9 +352,9 @@ __device__ __forceinline__ void row_chunk_stats(const void* rowp, int V, int chu
   const int v1 = min(sp.nvec, v0 + chunk_vecs);
   const int last = max(0, (sp.nvec + chunk_vecs - 1) / chunk_vecs - 1);
   if (T > 0.0f)
-    stats_sampling<DT>(rowp, sp, v0, v1, chunk == 0, chunk == last, c32_of(T), out);
+    stats_sampling<DT, NB>(rowp, sp, v0, v1, chunk == 0, chunk == last, c32_of(T), out);
   else
-    stats_greedy<DT>(rowp, sp, v0, v1, chunk == 0, chunk == last, out);
+    stats_greedy<DT, NB>(rowp, sp, v0, v1, chunk == 0, chunk == last, out);
 }
 
 }  // namespace sv
