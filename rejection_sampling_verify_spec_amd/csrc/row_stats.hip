@@ -84,12 +84,10 @@ hipError_t launch_row_stats(int dt, const void* tgt, const void* dft, int V, con
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   // Groups of loads in flight per thread: two (a whole 2048-vector chunk at
   // once; 78 VGPRs, six workgroups per CU for bf16) for the dense, tree and
-  // row layouts, one (57 VGPRs, eight per CU) for chunks of one group and for
-  // the ragged layout, where two
-  // measured slower, likely because its workgroups start with a dependent
-  // binary search of cu_gamma, which more resident workgroups cover. Measured
-  // on one box with two instead of one: large -1.4%, trees -1.0%, sampled
-  // rows -0.7%, ragged +1.3%. SPECVERIFY_STREAM_GROUPS (1 or 2) overrides.
+  // row layouts; one (57 VGPRs, eight per CU) for chunks of a single group and
+  // for the ragged layout, where two measured slower. Two instead of one,
+  // measured on one box: large -1.4%, trees -1.0%, sampled rows -0.7%,
+  // ragged +1.3%. SPECVERIFY_STREAM_GROUPS (1 or 2) overrides.
   static const int nb_env = [] {
     const char* e = getenv("SPECVERIFY_STREAM_GROUPS");
     const int v = e ? atoi(e) : 0;
