@@ -329,6 +329,17 @@ def test_tree_variants(sv):
     assert na[2] == -1 and (np.delete(na, 2) >= 0).all()
 
 
+def test_tree_temperature_extremes(sv):
+    """Lowest-child tree rule over temperatures from 1e-30 to 1e6 and over logits near the fp32
+    range (|max * log2(e)/T| far beyond 2^22)."""
+    d = inputgen.tree_inputs(32, 3000, seed=46, n_nodes=21, fanout=(4, 4, 1), dtype="f32", noise_sd=1.0,
+                             temperature=np.geomspace(1e-30, 1e6, 32).astype(np.float32))
+    _tree_check(sv, d, "tree T extremes")
+    d = inputgen.tree_inputs(8, 500, seed=47, n_nodes=10, fanout=(3, 2, 1), dtype="f32", scale=1e37, noise_sd=0.0,
+                             temperature=0.05)
+    _tree_check(sv, d, "tree overflowing offsets")
+
+
 def test_chain_shaped_tree_equals_chain(sv):
     d = inputgen.chain_inputs(32, 4, 3000, seed=51, dtype="bf16", scale=2.0, noise_sd=1.2)
     d["temperature"][::4] = 0.0

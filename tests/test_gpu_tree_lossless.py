@@ -73,6 +73,17 @@ def test_tree_variants(sv):
     assert na[2] == -1 and na[4] == -1 and (np.delete(na, [2, 4]) >= 0).all()
 
 
+def test_temperature_extremes(sv):
+    """The walk over temperatures from 1e-30 to 1e6 and over logits near the fp32 range."""
+    d = inputgen.tree_inputs(32, 3000, seed=79, n_nodes=21, fanout=(4, 4, 1), dtype="f32", noise_sd=1.0,
+                             temperature=np.geomspace(1e-30, 1e6, 32).astype(np.float32))
+    _, _, na = _check(sv, d, "T extremes")
+    assert (na >= 0).all()
+    d = inputgen.tree_inputs(8, 500, seed=81, n_nodes=10, fanout=(3, 2, 1), dtype="f32", scale=1e37, noise_sd=0.0,
+                             temperature=0.05)
+    _check(sv, d, "overflowing offsets")
+
+
 def test_chain_shaped_tree_equals_chain(sv):
     import torch
     d = inputgen.chain_inputs(32, 4, 3000, seed=78, dtype="bf16", scale=2.0, noise_sd=1.2)
