@@ -137,11 +137,16 @@ __device__ __forceinline__ void group_update(float& m, float& K, float& s, bool&
 // Block-wide merge of (m, s) in a fixed order; result valid in thread 0.
 __device__ __forceinline__ void block_merge_ms(float& m, float& s, float c, float* sm, float* ss) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // the wave maximum, each thread's sum rescaled to it once, then the wave
+  // sum (an empty thread has s = 0, a NaN-flagged one keeps its NaN)
+  float M = m;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    float m2 = __shfl_xor(m, off, 64), s2 = __shfl_xor(s, off, 64);
-    merge_ms(m, s, m2, s2, c);
-  }
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  float t = M == -INFINITY || m == M ? s : s * exp2_f32((m - M) * c);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
+  m = M;
+  s = t;
   if (lane == 0) { sm[wv] = m; ss[wv] = s; }
   wg_sync();
   if (threadIdx.x == 0) {
