@@ -34,18 +34,6 @@ __device__ __forceinline__ void wg_sync() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// OR of v over the workgroup (same result in every thread).
-__device__ __forceinline__ bool wg_or(bool v) {
-  __shared__ int flag[kTPB / 64];
-  const bool w = __ballot(v) != 0ull;
-  if ((threadIdx.x & 63) == 0) flag[threadIdx.x >> 6] = w;
-  wg_sync();
-  int any = 0;
-#pragma unroll
-  for (int k = 0; k < kTPB / 64; ++k) any |= flag[k];
-  return any != 0;
-}
-
 // Merge two (max, sum 2^{(x-max)c}) statistics.
 __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2, float c) {
   float M = fmaxf(m, m2);
@@ -134,11 +122,10 @@ __device__ __forceinline__ void group_update(float& m, float& K, float& s, bool&
   K = Kn;
 }
 
-// Block-wide merge of (m, s) in a fixed order; result valid in thread 0.
-__device__ __forceinline__ void block_merge_ms(float& m, float& s, float c, float* sm, float* ss) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  // the wave maximum, each thread's sum rescaled to it once, then the wave
-  // sum (an empty thread has s = 0, a NaN-flagged one keeps its NaN)
+// Wave-wide merge of (m, s): the wave maximum, each thread's sum rescaled to
+// it once, then the wave sum (an empty thread has s = 0, a NaN-flagged one
+// keeps its NaN); the result in every lane.
+__device__ __forceinline__ void wave_merge_ms(float& m, float& s, float c) {
   float M = m;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
@@ -147,12 +134,6 @@ __device__ __forceinline__ void block_merge_ms(float& m, float& s, float c, floa
   for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off, 64);
   m = M;
   s = t;
-  if (lane == 0) { sm[wv] = m; ss[wv] = s; }
-  wg_sync();
-  if (threadIdx.x == 0) {
-    m = sm[0]; s = ss[0];
-    for (int w = 1; w < kTPB / 64; ++w) merge_ms(m, s, sm[w], ss[w], c);
-  }
 }
 
 // Rare path of the sampling statistics: |max * c| >= 2^22 somewhere in the
@@ -219,13 +200,32 @@ __device__ __forceinline__ void sampling_finish(const void* rowp, const RowSplit
   // to the offset m c: 2^{x c - K} = 2^{(x - m) c} 2^{m c - K}
   if (m != -INFINITY && !ovf) s *= exp2_f32(-__builtin_fmaf(m, c, -K));
 
+  // the wave merges and the waves' overflow flags, exchanged over one barrier;
+  // then thread 0 merges the waves in a fixed order and publishes
   __shared__ float sm[kTPB / 64], ss[kTPB / 64];
-  const bool any_ovf = wg_or(ovf);
+  __shared__ int so[kTPB / 64];
+  const int lane = tid & 63, wv = tid >> 6;
+  wave_merge_ms(m, s, c);
+  const bool wovf = __ballot(ovf) != 0ull;
+  if (lane == 0) {
+    sm[wv] = m;
+    ss[wv] = s;
+    so[wv] = wovf;
+  }
+  wg_sync();
+  int any_ovf = 0;
+#pragma unroll
+  for (int k = 0; k < kTPB / 64; ++k) any_ovf |= so[k];
   if (!any_ovf) {
-    block_merge_ms(m, s, c, sm, ss);
-    if (tid == 0) publish_partial(out, sampling_partial(m, s));
+    if (tid == 0) {
+      m = sm[0];
+      s = ss[0];
+      for (int w = 1; w < kTPB / 64; ++w) merge_ms(m, s, sm[w], ss[w], c);
+      publish_partial(out, sampling_partial(m, s));
+    }
     return;
   }
+  // (m is now the wave maximum: the wide path only needs the block maximum)
   stats_sampling_wide<DT>(rowp, sp, v0, v1, do_head, do_tail, c, m, out, sm, ss);
 }
 
@@ -317,17 +317,20 @@ __device__ __forceinline__ void greedy_finish(const void* rowp, const RowSplit& 
     int i2 = __shfl_xor(idx, off, 64);
     if (m2 > m || (m2 == m && (unsigned)i2 < (unsigned)idx)) { m = m2; idx = i2; }
   }
+  // the waves' results and NaN flags over one barrier; thread 0 merges
   __shared__ float sm[kTPB / 64];
-  __shared__ int si[kTPB / 64];
-  const bool any_nan = wg_or(nan_seen);
-  if (lane == 0) { sm[wv] = m; si[wv] = idx; }
+  __shared__ int si[kTPB / 64], sn[kTPB / 64];
+  const bool wnan = __ballot(nan_seen) != 0ull;
+  if (lane == 0) { sm[wv] = m; si[wv] = idx; sn[wv] = wnan; }
   wg_sync();
   if (tid == 0) {
-    for (int w = 1; w < kTPB / 64; ++w)
+    bool any_nan = sn[0] != 0;
+    for (int w = 1; w < kTPB / 64; ++w) {
+      any_nan |= sn[w] != 0;
       if (sm[w] > m || (sm[w] == m && (unsigned)si[w] < (unsigned)idx)) { m = sm[w]; idx = si[w]; }
+    }
     publish_partial(out, greedy_partial(m, idx, any_nan || m == INFINITY));
   }
-  wg_sync();  // sm / si are reused by the workgroup's next chunk
 }
 
 template <int DT, int NB>
