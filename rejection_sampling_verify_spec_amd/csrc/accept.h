@@ -14,25 +14,45 @@ struct RowStat {
   bool ok;
 };
 
-// Running merge of a row's chunk partials, fed in ascending token order (so a
-// strict comparison keeps the lowest index of a tied maximum).
+// Running merge of a row's chunk partials, fed in blocks in ascending token
+// order.
 struct RowMerge {
   float M = -INFINITY;
   int idx = -1;
   bool bad = false;
   double Z = 0.0;
 
-  __device__ __forceinline__ void add(const Partial& q, double c, bool greedy) {
-    bad |= partial_bad(q, greedy);
-    const float s = partial_s(q);
-    if (q.m > M) {
-      // new running maximum: rescale what was summed so far
-      if (!greedy && M > -INFINITY) Z *= exp2_f64(((double)M - (double)q.m) * c);
-      M = q.m;
-      idx = partial_idx(q);
-      if (!greedy) Z += (double)s;
-    } else if (!greedy && q.m > -INFINITY) {
-      Z += (double)s * exp2_f64(((double)q.m - (double)M) * c);
+  // K partials at once, in ascending token order: their maximum first (a
+  // strict comparison keeps the lowest index of a tied maximum), then their
+  // sum rescaled to it term by term (independent exponentials), merged into
+  // the running statistic with at most one rescale.
+  template <int K>
+  __device__ __forceinline__ void add_block(const Partial (&q)[K], double c, bool greedy) {
+    float bm = -INFINITY;
+    int bi = -1;
+#pragma unroll
+    for (int u = 0; u < K; ++u) {
+      bad |= partial_bad(q[u], greedy);
+      if (q[u].m > bm) {
+        bm = q[u].m;
+        bi = partial_idx(q[u]);
+      }
+    }
+    if (bm == -INFINITY) return;  // nothing but empty chunks (or past the row)
+    double bz = 0.0;
+    if (!greedy) {
+#pragma unroll
+      for (int u = 0; u < K; ++u)
+        if (q[u].m > -INFINITY)
+          bz += (double)partial_s(q[u]) * (q[u].m == bm ? 1.0 : exp2_f64(((double)q[u].m - (double)bm) * c));
+    }
+    if (bm > M) {
+      if (!greedy && M > -INFINITY) Z *= exp2_f64(((double)M - (double)bm) * c);
+      M = bm;
+      idx = bi;
+      if (!greedy) Z += bz;
+    } else if (!greedy) {
+      Z += bz * exp2_f64(((double)bm - (double)M) * c);
     }
   }
 
@@ -64,8 +84,7 @@ __device__ __forceinline__ RowStat merge_row(const Partial* __restrict__ p, int 
   for (int k0 = 0; k0 < nchunk; k0 += K) {
     Partial q[K];
     load_partials<K>(p, nchunk, k0, true, q);
-#pragma unroll
-    for (int u = 0; u < K; ++u) r.add(q[u], c, greedy);  // past the row: {-inf, 1}, a no-op
+    r.add_block(q, c, greedy);  // past the row: {-inf, 1}, left out
   }
   return r.finish(greedy);
 }
@@ -80,11 +99,8 @@ __device__ __forceinline__ void merge_rows2(const Partial* __restrict__ p0, bool
     Partial q0[kMergeLoads], q1[kMergeLoads];
     load_partials<kMergeLoads>(p0, nchunk, k0, true, q0);
     load_partials<kMergeLoads>(p1, nchunk, k0, two, q1);
-#pragma unroll
-    for (int u = 0; u < kMergeLoads; ++u) {  // past the row (or no second row): {-inf, 1}, a no-op
-      a.add(q0[u], c, greedy0);
-      b.add(q1[u], c, false);
-    }
+    a.add_block(q0, c, greedy0);  // past the row (or no second row): {-inf, 1}, left out
+    b.add_block(q1, c, false);
   }
   r0 = a.finish(greedy0);
   r1 = b.finish(false);
