@@ -33,6 +33,7 @@ namespace sv {
 constexpr int kLLWaves = 12;  // three per SIMD: one workgroup fills a CU, so a team meets with few members
 constexpr int kLLThreads = kLLWaves * 64;
 constexpr int kLLMaxNodes = SV_MAX_TREE_NODES;
+constexpr int kLLSmallNodes = 128;  // trees up to this size keep most of the residual in LDS
 constexpr int kSpinPolls = 1 << 24;  // bound of one team wait (a few seconds of polls)
 
 struct LLArgs {
@@ -56,19 +57,21 @@ struct LLArgs {
   int32_t* num_acc;
 };
 
-// Shared memory of a workgroup (about 50 KB; one workgroup per CU).
+// Shared memory of a workgroup for trees of up to M nodes (about 50 KB at
+// 1024 nodes, 7 KB at 128; one workgroup per CU).
+template <int M>
 struct LLSpace {
-  int par[kLLMaxNodes], tok[kLLMaxNodes];
-  float mt[kLLMaxNodes];
+  int par[M], tok[M];
+  float mt[M];
   union {
-    float md[kLLMaxNodes];  // sampling: draft-row maxima
-    int idx[kLLMaxNodes];   // greedy: target-row argmax
+    float md[M];  // sampling: draft-row maxima
+    int idx[M];   // greedy: target-row argmax
   };
-  double zt[kLLMaxNodes], zd[kLLMaxNodes];
-  int kids[kLLMaxNodes];  // children of the current node, ascending (depths while the tree is checked)
-  int rej[kLLMaxNodes];   // its rejected children, in order (depths while the tree is checked)
-  unsigned char skip[kLLMaxNodes];  // 1 when that rejection's residual sum underflowed (r kept)
-  double S[kLLMaxNodes + 1];
+  double zt[M], zd[M];
+  int kids[M];  // children of the current node, ascending (depths while the tree is checked)
+  int rej[M];   // its rejected children, in order (depths while the tree is checked)
+  unsigned char skip[M];  // 1 when that rejection's residual sum underflowed (r kept)
+  double S[M + 1];
   double tab[64];
   int cnt[kLLWaves];
   int bad, flag, nk, wait_ok;
@@ -120,8 +123,8 @@ __device__ __forceinline__ double sum_segments(const double* buf, int nseg, int 
 // The logit that lane l of wave 0 needs for the test of child c after nrej
 // rejected siblings (l < nrej + 2 <= 64): the token's logit in the target row
 // (l = 0), in rejected sibling l's draft row, or in c's draft row (l = nrej + 1).
-template <int DT>
-__device__ __forceinline__ float child_logit(const LLArgs& A, const LLSpace& P, long long t0, long long d0, int v,
+template <int DT, class SP>
+__device__ __forceinline__ float child_logit(const LLArgs& A, const SP& P, long long t0, long long d0, int v,
                                              int nrej, int c, int l) {
   const int x = P.tok[c];
   if (l == 0) return Elem<DT>::at(A.tgt, (t0 + v) * (long long)A.V + x);
@@ -136,8 +139,8 @@ __device__ __forceinline__ float child_logit(const LLArgs& A, const LLSpace& P, 
 // probabilities; the residual steps are then applied in order across the
 // lanes (result in P.flag). With `pre`, lane l's logit of the first 64 was
 // loaded earlier (while the pass before this test ran): `lg`.
-template <int DT>
-__device__ __forceinline__ void child_test(const LLArgs& A, LLSpace& P, long long t0, long long d0, int v, int nrej,
+template <int DT, class SP>
+__device__ __forceinline__ void child_test(const LLArgs& A, SP& P, long long t0, long long d0, int v, int nrej,
                                            int c, double c64, bool pre = false, float lg = 0.0f) {
   const int tid = threadIdx.x, lane = tid & 63;
   if (tid < 64) {
@@ -171,7 +174,8 @@ __device__ __forceinline__ void child_test(const LLArgs& A, LLSpace& P, long lon
 }
 
 // Next rejected sibling at or after k whose residual step applies (nrej if none).
-__device__ __forceinline__ int next_live(const LLSpace& P, int k, int nrej) {
+template <class SP>
+__device__ __forceinline__ int next_live(const SP& P, int k, int nrej) {
   while (k < nrej && P.skip[k]) ++k;
   return k;
 }
@@ -181,18 +185,30 @@ __device__ __forceinline__ int next_live(const LLSpace& P, int k, int nrej) {
 template <int DT> struct Seg { static constexpr int tok = 64 * Elem<DT>::kPerVec; };
 constexpr int kSegBatch = 2;  // segments of one wave whose loads are in flight together
 
+// Segments whose residual a wave keeps in LDS (small trees): 12 KB per wave,
+// 144 KB for the workgroup's 12 waves. The rest go to the workspace.
+template <int DT> struct LdsSlots { static constexpr int n = 12288 / (Seg<DT>::tok * 8); };
+
+// LDS residual of one segment slot: token (lane*epv + e) of the segment at
+// double2 (e/2)*64 + lane, so that a wave's 16-byte accesses are consecutive.
+template <int DT>
+__device__ __forceinline__ double2* lds_slot(double2* base, int slot, int lane) {
+  return base + slot * (Seg<DT>::tok / 2) + lane;
+}
+
 // R at the lane's vector of up to kSegBatch segments (seg[i] < 0: none) of the
 // current node: R[i*epv + e] for token (seg[i]*64 + lane)*epv + e. The vectors
 // of one row are loaded together, and the next rejected sibling's row is in
 // flight while the current one is applied. With `rin` (the residual this wave
 // stored for the same segments in an earlier pass), R starts from it and only
 // the steps step_from .. nrej-1 are applied: the same operations in the same
-// order as from the rows, so the same values.
-template <int DT>
-__device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P, const char* trow, long long d0,
+// order as from the rows, so the same values. The wave's segments j0 + i below
+// kSlots hold that residual in LDS (`lres`), the others at `rin`.
+template <int DT, int kSlots, class SP>
+__device__ __forceinline__ void residual_segs(const LLArgs& A, const SP& P, const char* trow, long long d0,
                                               int v, int nrej, const int (&seg)[kSegBatch], int lane, double c64,
                                               double (&R)[kSegBatch * Elem<DT>::kPerVec], const double* rin = nullptr,
-                                              int step_from = 0) {
+                                              int step_from = 0, double2* lres = nullptr, int j0 = 0) {
   constexpr int epv = Elem<DT>::kPerVec;
   constexpr int es = sizeof(typename Elem<DT>::T);
   auto drow = [&](int k) {
@@ -215,6 +231,16 @@ __device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P,
   if (rin) {
 #pragma unroll
     for (int i = 0; i < kSegBatch; ++i) {
+      if (j0 + i < kSlots) {  // (uniform)
+        const double2* src = lds_slot<DT>(lres, j0 + i, lane);
+#pragma unroll
+        for (int q = 0; q < epv / 2; ++q) {
+          const double2 v2 = src[q * 64];
+          R[i * epv + 2 * q] = seg[i] < 0 ? 0.0 : v2.x;
+          R[i * epv + 2 * q + 1] = seg[i] < 0 ? 0.0 : v2.y;
+        }
+        continue;
+      }
       const double2* src =
           reinterpret_cast<const double2*>(rin + (size_t)(seg[i] < 0 ? 0 : seg[i]) * Seg<DT>::tok + lane * epv);
 #pragma unroll
@@ -264,27 +290,36 @@ __device__ __forceinline__ void residual_segs(const LLArgs& A, const LLSpace& P,
 // A wave takes the same segments in every pass, so it can keep R for them:
 // with `rin`, R is its stored residual plus the steps step_from .. nrej-1
 // (one new rejected sibling's row instead of all of them), else it is formed
-// from the rows; with `rout`, the new R is stored there.
-template <int DT>
-__device__ bool team_pass(const LLArgs& A, LLSpace& P, long long t0, long long d0, int v, int nrej, double* buf,
+// from the rows; with `rout`, the new R is stored there. The wave's first
+// kSlots segments keep R in its LDS region `lres` instead, updated in place
+// (only this wave reads them, and it reads a segment before it writes it).
+template <int DT, int kSlots, class SP>
+__device__ bool team_pass(const LLArgs& A, SP& P, long long t0, long long d0, int v, int nrej, double* buf,
                           int* ctr, int target, int rank, double c64, const double* rin, int step_from,
-                          double* rout) {
+                          double* rout, double2* lres) {
   constexpr int epv = Elem<DT>::kPerVec;
   constexpr int es = sizeof(typename Elem<DT>::T);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // (uniform: segment indices in scalar registers)
   const int nw = A.G * kLLWaves;
   const char* trow = reinterpret_cast<const char*>(A.tgt) + (size_t)(t0 + v) * (size_t)A.V * es;
-  for (int s0 = rank * kLLWaves + wv; s0 < A.nseg; s0 += nw * kSegBatch) {
+  int j0 = 0;  // the wave's index of segment s0 among its own segments
+  for (int s0 = rank * kLLWaves + wv; s0 < A.nseg; s0 += nw * kSegBatch, j0 += kSegBatch) {
     int seg[kSegBatch];
 #pragma unroll
     for (int i = 0; i < kSegBatch; ++i) seg[i] = s0 + i * nw < A.nseg ? s0 + i * nw : -1;
     double R[kSegBatch * epv];
-    residual_segs<DT>(A, P, trow, d0, v, nrej, seg, lane, c64, R, rin, step_from);
+    residual_segs<DT, kSlots>(A, P, trow, d0, v, nrej, seg, lane, c64, R, rin, step_from, lres, j0);
     if (rout) {
 #pragma unroll
       for (int i = 0; i < kSegBatch; ++i) {
         if (seg[i] < 0) continue;
+        if (j0 + i < kSlots) {
+          double2* dst = lds_slot<DT>(lres, j0 + i, lane);
+#pragma unroll
+          for (int q = 0; q < epv / 2; ++q) dst[q * 64] = make_double2(R[i * epv + 2 * q], R[i * epv + 2 * q + 1]);
+          continue;
+        }
         double* dst = rout + (size_t)seg[i] * Seg<DT>::tok + lane * epv;
 #pragma unroll
         for (int e = 0; e < epv; ++e) dst[e] = R[i * epv + e];
@@ -322,7 +357,8 @@ __device__ bool team_pass(const LLArgs& A, LLSpace& P, long long t0, long long d
 }
 
 // Children of node v in ascending index order into P.kids / P.nk.
-__device__ __forceinline__ void list_children(LLSpace& P, int N, int v) {
+template <class SP>
+__device__ __forceinline__ void list_children(SP& P, int N, int v) {
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   int base = 0;
   for (int c0 = 1; c0 < N; c0 += kLLThreads) {
@@ -344,8 +380,8 @@ __device__ __forceinline__ void list_children(LLSpace& P, int N, int v) {
 // The inverse-CDF pick of the final token by wave 0 of the team's first
 // workgroup: the segment whose running sum first exceeds u * S, then the token
 // in it; the last token of positive mass when rounding leaves none.
-template <int DT>
-__device__ int pick_token(const LLArgs& A, LLSpace& P, long long t0, long long d0, int v, int nrej,
+template <int DT, class SP>
+__device__ int pick_token(const LLArgs& A, SP& P, long long t0, long long d0, int v, int nrej,
                           const double* buf, double thr, double c64, int lane) {
   constexpr int epv = Elem<DT>::kPerVec;
   // the segment
@@ -383,7 +419,7 @@ __device__ int pick_token(const LLArgs& A, LLSpace& P, long long t0, long long d
 #pragma unroll
   for (int i = 1; i < kSegBatch; ++i) seg[i] = -1;
   double R[kSegBatch * epv];
-  residual_segs<DT>(A, P, trow, d0, v, nrej, seg, lane, c64, R);
+  residual_segs<DT, 0>(A, P, trow, d0, v, nrej, seg, lane, c64, R);
   const int jl = (sg * 64 + lane) * epv;
   double s = 0.0;
 #pragma unroll
@@ -413,10 +449,15 @@ __device__ int pick_token(const LLArgs& A, LLSpace& P, long long t0, long long d
   return y >= 0 ? y : ylast;
 }
 
-template <int DT>
+// kSmall: trees of up to kLLSmallNodes nodes, with the residual of each wave's
+// first segments in LDS.
+template <int DT, bool kSmall>
 __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_tree_lossless(LLArgs A) {
-  __shared__ LLSpace P;
+  __shared__ LLSpace<kSmall ? kLLSmallNodes : kLLMaxNodes> P;
+  constexpr int kSlots = kSmall ? LdsSlots<DT>::n : 0;
+  __shared__ double2 RL[kSmall ? kLLWaves * kSlots * Seg<DT>::tok / 2 : 1];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  double2* const lres = kSlots ? RL + __builtin_amdgcn_readfirstlane(wv) * kSlots * (Seg<DT>::tok / 2) : nullptr;
   // a team's workgroups on one XCD when the teams fill whole XCD rounds
   // (workgroup i of the grid runs on XCD i mod 8)
   const JobPart jp = A.nteams % kXcds == 0 ? xcd_job_part(blockIdx.x, A.G) : JobPart{(int)blockIdx.x / A.G, (int)blockIdx.x % A.G};
@@ -552,8 +593,8 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
         if (pre && tid < 64) lg = child_logit<DT>(A, P, t0, d0, v, nrej, P.kids[i + 1], lane);
         const double* rin = P.have_store ? rbuf + (size_t)P.eff * slab : nullptr;
         double* rout = rbuf + (size_t)(1 - P.eff) * slab;
-        if (!team_pass<DT>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr, passes * A.G, rank,
-                           c64, rin, nrej - 1, rout)) {
+        if (!team_pass<DT, kSlots>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr, passes * A.G,
+                                   rank, c64, rin, nrej - 1, rout, lres)) {
           failed = true;
           break;
         }
@@ -570,10 +611,12 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
         }
         __syncthreads();
         have_sums = !P.skip[nrej - 1];
-        // the new residual is the current one unless its sum underflowed (r kept)
-        if (tid == 0 && have_sums) {
-          P.eff = 1 - P.eff;
-          P.have_store = 1;
+        // the new residual is the current one unless its sum underflowed (r
+        // kept); then the LDS part holds the discarded one, and the next pass
+        // forms R from the rows again
+        if (tid == 0) {
+          if (have_sums) P.eff = 1 - P.eff;
+          P.have_store = have_sums ? 1 : 0;
         }
         __syncthreads();
       }
@@ -588,8 +631,9 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
     }
     if (!failed && !have_sums) {
       ++passes;
-      failed = !team_pass<DT>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr, passes * A.G,
-                              rank, c64, P.have_store ? rbuf + (size_t)P.eff * slab : nullptr, nrej, nullptr);
+      failed = !team_pass<DT, kSlots>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr,
+                                      passes * A.G, rank, c64, P.have_store ? rbuf + (size_t)P.eff * slab : nullptr,
+                                      nrej, nullptr, lres);
     }
     if (failed) {
       // a team wait ran out of polls: this team's remaining requests report -1
@@ -626,8 +670,11 @@ hipError_t launch_tree_lossless(int dt, const void* tgt, const void* dft, int V,
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 1;
-  const void* fn = dt == 1 ? reinterpret_cast<const void*>(&k_tree_lossless<1>)
-                           : reinterpret_cast<const void*>(&k_tree_lossless<0>);
+  const bool small = L.gamma <= kLLSmallNodes;
+  const void* fn = dt == 1 ? (small ? reinterpret_cast<const void*>(&k_tree_lossless<1, true>)
+                                    : reinterpret_cast<const void*>(&k_tree_lossless<1, false>))
+                           : (small ? reinterpret_cast<const void*>(&k_tree_lossless<0, true>)
+                                    : reinterpret_cast<const void*>(&k_tree_lossless<0, false>));
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kLLThreads, 0);
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorInvalidConfiguration;

@@ -64,6 +64,10 @@ def test_tree_variants(sv):
            "1023 siblings")
     _check(sv, inputgen.tree_inputs(8, 600_001, seed=80, n_nodes=21, fanout=(4, 4, 1), dtype="bf16", noise_sd=1.5),
            "V=600001")
+    # fp32 rows of 782 segments over 96 waves: each wave keeps 6 segments' residual in LDS, the rest
+    # in the workspace
+    _check(sv, inputgen.tree_inputs(32, 200_003, seed=82, n_nodes=21, fanout=(4, 4, 1), dtype="f32",
+                                    iid_draft=True), "f32 V=200003, iid drafts")
     bad = inputgen.tree_inputs(6, 100, seed=77, n_nodes=10, fanout=(3, 2, 1), dtype="f32")
     bad["parents"] = bad["parents"].copy()
     bad["parents"][2, 5] = 7
