@@ -572,6 +572,8 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
         P.eff = 0;
         P.have_store = 0;  // a new node: no stored residual yet
       }
+      // (every wave reads this state next: at a leaf, in the final pass)
+      __syncthreads();
       nrej = 0;
       have_sums = false;
       int accepted = -1;
