@@ -645,11 +645,16 @@ def run_bench(args):
 
 # Pooled parity: seeds 1000 + k of a workload until at least 10^4 requests (the near-tie rate of
 # the parity bar is a fraction of requests, so it needs that many to be measured at all)
-POOL_SEEDS = {"tiny": 1250, "mid": 157, "large": 40, "ragged": 10, "tree_near": 40}
+POOL_SEEDS = {"tiny": 1250, "mid": 157, "large": 40, "ragged": 10, "tree_near": 40, "tree_rule": 40,
+              "tree_walk": 40}
 FLAG = 1e-5
 # tree_near: lossless multi-candidate trees with near-identical drafts and forced rejections, 250
 # trees of V=30000 per seed; seed k takes case k % 4 (dtype, noise of the draft rows)
 NEAR_CASES = (("f32", 0.003), ("f32", 0.01), ("f32", 0.03), ("bf16", 0.05))
+# tree_rule / tree_walk: the lowest-child rule and the lossless walk on 64-node trees (4 children of
+# the root, 4 under each, 2-3 under those), 250 trees of V=10007 per seed; seed k takes case k % 4
+# (dtype, noise of the draft rows, temperature)
+TREE_CASES = (("bf16", 0.7, 1.0), ("f32", 1.5, 0.8), ("bf16", 0.3, 1.2), ("f32", 3.0, 0.6))
 
 
 def pooled_inputs(name, seed):
@@ -658,6 +663,10 @@ def pooled_inputs(name, seed):
     if name == "tree_near":
         dtype, noise = NEAR_CASES[(seed - 1000) % len(NEAR_CASES)]
         return inputgen.near_identical_trees(250, 30000, seed, dtype=dtype, noise_sd=noise), "tree_lossless"
+    if name in ("tree_rule", "tree_walk"):
+        dtype, noise, temp = TREE_CASES[(seed - 1000) % len(TREE_CASES)]
+        d = inputgen.tree_inputs(250, 10007, seed, dtype=dtype, noise_sd=noise, temperature=temp)
+        return d, "tree" if name == "tree_rule" else "tree_lossless"
     return inputgen.make(name, seed=seed), name
 
 
@@ -837,8 +846,8 @@ def main():
                     help="do not create the library's kernel events (profiling runs: the profiler times the kernels)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pooled-parity", metavar="NAMES",
-                    help="comma-separated workloads (tiny,mid,large,ragged,tree_near): GPU against the oracle over many "
-                         "seeds")
+                    help="comma-separated workloads (tiny,mid,large,ragged,tree_near,tree_rule,tree_walk): "
+                         "GPU against the oracle over many seeds")
     ap.add_argument("--pool-seeds", type=int, default=None, help="seeds per workload for --pooled-parity")
     ap.add_argument("--summarize-rocprof", metavar="DIR")
     ap.add_argument("--write-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
