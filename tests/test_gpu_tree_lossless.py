@@ -77,6 +77,20 @@ def test_tree_variants(sv):
     assert na[2] == -1 and na[4] == -1 and (np.delete(na, [2, 4]) >= 0).all()
 
 
+def test_teams_loop_over_requests(sv):
+    """More requests than resident teams (one workgroup per team at this batch size): a team walks
+    several requests in turn, reusing its shared state and its LDS residual; mixed dtypes and
+    temperatures, greedy requests among them."""
+    d = inputgen.tree_inputs(600, 1500, seed=83, n_nodes=21, fanout=(4, 4, 1), dtype="bf16", noise_sd=1.0,
+                             temperature=0.9)
+    d["temperature"][::5] = 0.0
+    _, _, na = _check(sv, d, "600 requests bf16")
+    assert (na >= 0).all()
+    d = inputgen.tree_inputs(520, 2100, seed=84, n_nodes=21, fanout=(4, 4, 1), dtype="f32", iid_draft=True)
+    _, _, na = _check(sv, d, "520 requests f32, iid drafts")
+    assert (na >= 0).all()
+
+
 def test_temperature_extremes(sv):
     """The walk over temperatures from 1e-30 to 1e6 and over logits near the fp32 range."""
     d = inputgen.tree_inputs(32, 3000, seed=79, n_nodes=21, fanout=(4, 4, 1), dtype="f32", noise_sd=1.0,
