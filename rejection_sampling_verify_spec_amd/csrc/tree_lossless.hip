@@ -190,7 +190,8 @@ constexpr int kSegBatch = 2;  // segments of one wave whose loads are in flight 
 template <int DT> struct LdsSlots { static constexpr int n = 12288 / (Seg<DT>::tok * 8); };
 
 // LDS residual of one segment slot: token (lane*epv + e) of the segment at
-// double2 (e/2)*64 + lane, so that a wave's 16-byte accesses are consecutive.
+// double2 (e/2)*64 + lane of the slot, component e % 2, so that a wave's
+// 16-byte accesses are consecutive.
 template <int DT>
 __device__ __forceinline__ double2* lds_slot(double2* base, int slot, int lane) {
   return base + slot * (Seg<DT>::tok / 2) + lane;
