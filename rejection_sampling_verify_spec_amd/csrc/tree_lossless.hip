@@ -186,15 +186,27 @@ template <int DT> struct Seg { static constexpr int tok = 64 * Elem<DT>::kPerVec
 constexpr int kSegBatch = 2;  // segments of one wave whose loads are in flight together
 
 // Segments whose residual a wave keeps in LDS (small trees): 12 KB per wave,
-// 144 KB for the workgroup's 12 waves. The rest go to the workspace.
+// 144 KB for the workgroup's 12 waves, and 8 KB more as one extra segment for
+// each of the workgroup's first waves (the waves that hold one segment more
+// than the others when a row's segments do not divide evenly). The rest go to
+// the workspace.
 template <int DT> struct LdsSlots { static constexpr int n = 12288 / (Seg<DT>::tok * 8); };
+template <int DT> struct LdsExtra { static constexpr int n = 8192 / (Seg<DT>::tok * 8); };
+
+// A wave's LDS residual: slots 0 .. LdsSlots-1 in its own region, slot
+// LdsSlots (when n says so) from the workgroup's extra segments.
+struct LdsRes {
+  double2* base;   // the wave's region (none when n == 0)
+  double2* extra;  // its extra segment (none when n <= LdsSlots)
+  int n;           // segments held in LDS
+};
 
 // LDS residual of one segment slot: token (lane*epv + e) of the segment at
 // double2 (e/2)*64 + lane of the slot, component e % 2, so that a wave's
 // 16-byte accesses are consecutive.
 template <int DT>
-__device__ __forceinline__ double2* lds_slot(double2* base, int slot, int lane) {
-  return base + slot * (Seg<DT>::tok / 2) + lane;
+__device__ __forceinline__ double2* lds_slot(const LdsRes& L, int slot, int lane) {
+  return (slot < LdsSlots<DT>::n ? L.base + slot * (Seg<DT>::tok / 2) : L.extra) + lane;
 }
 
 // R at the lane's vector of up to kSegBatch segments (seg[i] < 0: none) of the
@@ -204,12 +216,13 @@ __device__ __forceinline__ double2* lds_slot(double2* base, int slot, int lane) 
 // stored for the same segments in an earlier pass), R starts from it and only
 // the steps step_from .. nrej-1 are applied: the same operations in the same
 // order as from the rows, so the same values. The wave's segments j0 + i below
-// kSlots hold that residual in LDS (`lres`), the others at `rin`.
-template <int DT, int kSlots, class SP>
+// lres.n hold that residual in LDS, the others at `rin`.
+template <int DT, class SP>
 __device__ __forceinline__ void residual_segs(const LLArgs& A, const SP& P, const char* trow, long long d0,
                                               int v, int nrej, const int (&seg)[kSegBatch], int lane, double c64,
                                               double (&R)[kSegBatch * Elem<DT>::kPerVec], const double* rin = nullptr,
-                                              int step_from = 0, double2* lres = nullptr, int j0 = 0) {
+                                              int step_from = 0, const LdsRes& lres = LdsRes{nullptr, nullptr, 0},
+                                              int j0 = 0) {
   constexpr int epv = Elem<DT>::kPerVec;
   constexpr int es = sizeof(typename Elem<DT>::T);
   auto drow = [&](int k) {
@@ -232,7 +245,7 @@ __device__ __forceinline__ void residual_segs(const LLArgs& A, const SP& P, cons
   if (rin) {
 #pragma unroll
     for (int i = 0; i < kSegBatch; ++i) {
-      if (j0 + i < kSlots) {  // (uniform)
+      if (j0 + i < lres.n) {  // (uniform)
         const double2* src = lds_slot<DT>(lres, j0 + i, lane);
 #pragma unroll
         for (int q = 0; q < epv / 2; ++q) {
@@ -292,12 +305,15 @@ __device__ __forceinline__ void residual_segs(const LLArgs& A, const SP& P, cons
 // with `rin`, R is its stored residual plus the steps step_from .. nrej-1
 // (one new rejected sibling's row instead of all of them), else it is formed
 // from the rows; with `rout`, the new R is stored there. The wave's first
-// kSlots segments keep R in its LDS region `lres` instead, updated in place
-// (only this wave reads them, and it reads a segment before it writes it).
-template <int DT, int kSlots, class SP>
+// lres.n segments keep R in LDS instead, updated in place (only this wave
+// reads them, and it reads a segment before it writes it). Wave w of
+// workgroup `rank` takes segments w G + rank + j nw, j = 0, 1, ...: where the
+// segments do not divide evenly, the waves with one more are spread over the
+// workgroups (their first waves) rather than gathered in one.
+template <int DT, class SP>
 __device__ bool team_pass(const LLArgs& A, SP& P, long long t0, long long d0, int v, int nrej, double* buf,
                           int* ctr, int target, int rank, double c64, const double* rin, int step_from,
-                          double* rout, double2* lres) {
+                          double* rout, const LdsRes& lres) {
   constexpr int epv = Elem<DT>::kPerVec;
   constexpr int es = sizeof(typename Elem<DT>::T);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -305,17 +321,17 @@ __device__ bool team_pass(const LLArgs& A, SP& P, long long t0, long long d0, in
   const int nw = A.G * kLLWaves;
   const char* trow = reinterpret_cast<const char*>(A.tgt) + (size_t)(t0 + v) * (size_t)A.V * es;
   int j0 = 0;  // the wave's index of segment s0 among its own segments
-  for (int s0 = rank * kLLWaves + wv; s0 < A.nseg; s0 += nw * kSegBatch, j0 += kSegBatch) {
+  for (int s0 = wv * A.G + rank; s0 < A.nseg; s0 += nw * kSegBatch, j0 += kSegBatch) {
     int seg[kSegBatch];
 #pragma unroll
     for (int i = 0; i < kSegBatch; ++i) seg[i] = s0 + i * nw < A.nseg ? s0 + i * nw : -1;
     double R[kSegBatch * epv];
-    residual_segs<DT, kSlots>(A, P, trow, d0, v, nrej, seg, lane, c64, R, rin, step_from, lres, j0);
+    residual_segs<DT>(A, P, trow, d0, v, nrej, seg, lane, c64, R, rin, step_from, lres, j0);
     if (rout) {
 #pragma unroll
       for (int i = 0; i < kSegBatch; ++i) {
         if (seg[i] < 0) continue;
-        if (j0 + i < kSlots) {
+        if (j0 + i < lres.n) {
           double2* dst = lds_slot<DT>(lres, j0 + i, lane);
 #pragma unroll
           for (int q = 0; q < epv / 2; ++q) dst[q * 64] = make_double2(R[i * epv + 2 * q], R[i * epv + 2 * q + 1]);
@@ -420,7 +436,7 @@ __device__ int pick_token(const LLArgs& A, SP& P, long long t0, long long d0, in
 #pragma unroll
   for (int i = 1; i < kSegBatch; ++i) seg[i] = -1;
   double R[kSegBatch * epv];
-  residual_segs<DT, 0>(A, P, trow, d0, v, nrej, seg, lane, c64, R);
+  residual_segs<DT>(A, P, trow, d0, v, nrej, seg, lane, c64, R);
   const int jl = (sg * 64 + lane) * epv;
   double s = 0.0;
 #pragma unroll
@@ -456,9 +472,14 @@ template <int DT, bool kSmall>
 __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_tree_lossless(LLArgs A) {
   __shared__ LLSpace<kSmall ? kLLSmallNodes : kLLMaxNodes> P;
   constexpr int kSlots = kSmall ? LdsSlots<DT>::n : 0;
-  __shared__ double2 RL[kSmall ? kLLWaves * kSlots * Seg<DT>::tok / 2 : 1];
+  constexpr int kExtra = kSmall ? LdsExtra<DT>::n : 0;
+  constexpr int kS2 = Seg<DT>::tok / 2;  // double2 per segment
+  __shared__ double2 RL[kSmall ? (kLLWaves * kSlots + kExtra) * kS2 : 1];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  double2* const lres = kSlots ? RL + __builtin_amdgcn_readfirstlane(wv) * kSlots * (Seg<DT>::tok / 2) : nullptr;
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  const LdsRes lres = kSmall ? LdsRes{RL + wvu * kSlots * kS2, wvu < kExtra ? RL + (kLLWaves * kSlots + wvu) * kS2 : nullptr,
+                                      kSlots + (wvu < kExtra ? 1 : 0)}
+                             : LdsRes{nullptr, nullptr, 0};
   // a team's workgroups on one XCD when the teams fill whole XCD rounds
   // (workgroup i of the grid runs on XCD i mod 8)
   const JobPart jp = A.nteams % kXcds == 0 ? xcd_job_part(blockIdx.x, A.G) : JobPart{(int)blockIdx.x / A.G, (int)blockIdx.x % A.G};
@@ -596,7 +617,7 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
         if (pre && tid < 64) lg = child_logit<DT>(A, P, t0, d0, v, nrej, P.kids[i + 1], lane);
         const double* rin = P.have_store ? rbuf + (size_t)P.eff * slab : nullptr;
         double* rout = rbuf + (size_t)(1 - P.eff) * slab;
-        if (!team_pass<DT, kSlots>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr, passes * A.G,
+        if (!team_pass<DT>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr, passes * A.G,
                                    rank, c64, rin, nrej - 1, rout, lres)) {
           failed = true;
           break;
@@ -634,7 +655,7 @@ __global__ __launch_bounds__(kLLThreads) __attribute__((amdgpu_waves_per_eu(3)))
     }
     if (!failed && !have_sums) {
       ++passes;
-      failed = !team_pass<DT, kSlots>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr,
+      failed = !team_pass<DT>(A, P, t0, d0, v, nrej, sums + (size_t)(passes & 1) * A.nseg, ctr,
                                       passes * A.G, rank, c64, P.have_store ? rbuf + (size_t)P.eff * slab : nullptr,
                                       nrej, nullptr, lres);
     }
