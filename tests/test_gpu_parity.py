@@ -264,6 +264,27 @@ def test_ragged_full_size(sv):
     _ragged_check(sv, inputgen.make("ragged"), "ragged full")
 
 
+def test_ragged_mid_batches(sv):
+    """600 requests (gamma_b 0..8, odd V, greedy requests; more tail workgroups than are resident at
+    once) and 256 (fp32)."""
+    d = inputgen.ragged_inputs(600, 0, 8, 3001, seed=24, dtype="bf16", n_greedy=100)
+    _ragged_check(sv, d, "ragged 600 bf16")
+    d = inputgen.ragged_inputs(256, 1, 6, 2000, seed=25, dtype="f32", n_greedy=40)
+    _ragged_check(sv, d, "ragged 256 f32")
+
+
+def test_ragged_bad_layout_large_batch(sv):
+    """A malformed cu_gamma in a batch of 300: every request fails (-1)."""
+    d = inputgen.ragged_inputs(300, 1, 4, 300, seed=26, dtype="f32")
+    d["cu_gamma"] = d["cu_gamma"].copy()
+    d["cu_gamma"][150] = d["cu_gamma"][151] + 3
+    t = device_inputs(d)
+    out, na = sv.verify_ragged(t["target"], t["draft"], t["cu_gamma"], d["total_draft"], t["draft_tokens"],
+                               t["u_accept"], t["u_sample"], t["temperature"], d["gamma_max"])
+    _sync()
+    assert (na.cpu().numpy() == -1).all() and (out.cpu().numpy() == -1).all()
+
+
 def test_ragged_bad_layout(sv):
     d = inputgen.ragged_inputs(16, 1, 4, 300, seed=23, dtype="f32")
     d["cu_gamma"] = d["cu_gamma"].copy()
