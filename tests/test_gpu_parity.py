@@ -296,6 +296,18 @@ def test_ragged_bad_layout(sv):
     assert (na.cpu().numpy() == -1).all() and (out.cpu().numpy() == -1).all()
 
 
+def test_tree_tiny_vocab(sv):
+    """Rows shorter than one 16-byte vector or one tile (V = 1 .. 17, bf16 rows off the 16-byte grid),
+    every fourth tree greedy."""
+    for V in (1, 3, 7, 9, 17):
+        for dtype in ("f32", "bf16"):
+            d = inputgen.tree_inputs(12, V, seed=900 + V, n_nodes=10, fanout=(3, 2, 1), dtype=dtype, noise_sd=1.0,
+                                     temperature=0.8)
+            d["temperature"][::4] = 0.0
+            na = _tree_check(sv, d, f"tree V={V} {dtype}")
+            assert (na >= 0).all()
+
+
 def test_dense_equals_ragged(sv):
     import torch
     d = inputgen.chain_inputs(40, 5, 7000, seed=31, dtype="bf16", scale=3.0, noise_sd=1.0)

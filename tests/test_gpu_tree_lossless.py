@@ -77,6 +77,18 @@ def test_tree_variants(sv):
     assert na[2] == -1 and na[4] == -1 and (np.delete(na, [2, 4]) >= 0).all()
 
 
+def test_tiny_vocab(sv):
+    """Rows shorter than one 16-byte vector or one segment (V = 1 .. 17, bf16 rows off the 16-byte
+    grid), every fourth tree greedy."""
+    for V in (1, 3, 7, 9, 17):
+        for dtype in ("f32", "bf16"):
+            d = inputgen.tree_inputs(12, V, seed=900 + V, n_nodes=10, fanout=(3, 2, 1), dtype=dtype, noise_sd=1.0,
+                                     temperature=0.8)
+            d["temperature"][::4] = 0.0
+            _, _, na = _check(sv, d, f"lossless V={V} {dtype}")
+            assert (na >= 0).all()
+
+
 def test_teams_loop_over_requests(sv):
     """More requests than resident teams (one workgroup per team at this batch size): a team walks
     several requests in turn, reusing its shared state and its LDS residual; mixed dtypes and
