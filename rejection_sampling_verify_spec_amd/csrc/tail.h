@@ -193,10 +193,6 @@ __device__ __forceinline__ uint64_t rec_load(const TileRec* R, int word) {
   return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<TileRec*>(R)) + word, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ double rec_f64(const TileRec* R, int word) {
-  return __longlong_as_double((long long)rec_load(R, word));
-}
-__device__ __forceinline__ int rec_ngrp(const TileRec* R) { return (int)(uint32_t)rec_load(R, kRecNgrp); }
 __device__ __forceinline__ uint64_t f64_word(double v) { return (uint64_t)__double_as_longlong(v); }
 __device__ __forceinline__ uint64_t ngrp_word(int ng) { return (uint64_t)(uint32_t)ng; }
 
